@@ -1,0 +1,175 @@
+"""Reference implementations in float64 -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's ``cpu_baseline``
+leg may import this module.  The product path never does, and nothing here is
+shared with the HIP library.
+
+Three references, each a plain reading of the pages:
+
+* ``attention_f64`` -- the definition of exact attention (scores, three-pass safe
+  softmax, P*V, logsumexp), computed by the C library ``liboracle.so`` built from
+  ``attn_ref.c`` with the whole score row materialised.
+* ``softmax_3pass`` / ``online_softmax`` -- the safe softmax as three passes, and the
+  running-max / running-sum recurrence that replaces the first two passes.
+* ``flash_attention2_tiled`` -- the FlashAttention-2 forward algorithm step by step
+  (Q blocks outside, K/V blocks inside, running m and l, unnormalised output, one
+  division at the end, logsumexp), used to show on the CPU that the tiled method
+  reaches the definition's result.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.build(force=False)
+        lib = ctypes.CDLL(path)
+        lib.oracle_attention_f64.restype = ctypes.c_int
+        lib.oracle_attention_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        _LIB = lib
+    return _LIB
+
+
+def attention_f64(q, k, v, scale, causal, rows=None, nthreads=None):
+    """Exact attention in float64 by its definition.
+
+    Follows "Flash Attention 全解析（上）" section 1.2 (S = QK^T, safe softmax in
+    three passes, O = PV) and the logsumexp L = m + log(l) of "FlashAttention 怎么做?
+    online softmax 怎么更新?" (section "FlashAttention-2 改了什么").
+
+    q: [B, H, Lq, d]; k, v: [B, H, Lk, d] -- any real dtype, widened to float64.
+    scale: the scale the device uses (an fp32 value is widened exactly).
+    causal: key j visible to query i iff j <= i (top-left alignment).
+    rows: None for every query row, else an int array [B*H, n] (or [n], shared by
+          every head) of query indices to compute.
+    Returns (o, lse): o [B, H, n, d], lse [B, H, n] in float64.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    assert k.shape == (B, H, Lk, d) and v.shape == (B, H, Lk, d)
+    if rows is None:
+        nr = Lq
+        rows_arr = None
+    else:
+        rows_arr = np.asarray(rows, dtype=np.int64)
+        if rows_arr.ndim == 1:
+            rows_arr = np.broadcast_to(rows_arr, (B * H, rows_arr.shape[0]))
+        rows_arr = np.ascontiguousarray(rows_arr.reshape(B * H, -1), dtype=np.int64)
+        nr = rows_arr.shape[1]
+    o = np.empty((B, H, nr, d), dtype=np.float64)
+    lse = np.empty((B, H, nr), dtype=np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    rc = _lib().oracle_attention_f64(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data,
+        B, H, Lq, Lk, d, float(scale), int(bool(causal)),
+        rows_arr.ctypes.data if rows_arr is not None else None, nr,
+        o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attention_f64 rejected its arguments (code %d)" % rc)
+    return o, lse
+
+
+def softmax_3pass(x):
+    """Safe softmax of a 1-D row in three passes: max, sum of exp(x - m), divide.
+
+    "Flash Attention 全解析（上）" section 1.2, the three-pass safe softmax.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m = -np.inf
+    for xi in x:                      # pass 1: running max over the whole row
+        m = max(m, xi)
+    l = 0.0
+    for xi in x:                      # pass 2: denominator with the final max
+        l += np.exp(xi - m)
+    return np.array([np.exp(xi - m) / l for xi in x])  # pass 3
+
+
+def online_softmax(x, block=1):
+    """Online softmax of a 1-D row, block by block.
+
+    The running max m and the running sum l are updated together; when a block
+    raises the max, the old sum is multiplied by exp(m_old - m_new).  A second
+    pass divides exp(x - m_final) by l_final.  "Flash Attention 全解析（上）"
+    section 2.2.1 (block = 1) and "FlashAttention 怎么做? online softmax 怎么更新?"
+    section "Online softmax" (the worked row (1, 3 | 2, 5) uses block = 2).
+
+    Returns (p, trace) where trace[b] = (m, l) after block b.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, l = -np.inf, 0.0
+    trace = []
+    for start in range(0, len(x), block):
+        blk = x[start:start + block]
+        m_new = max(m, float(blk.max()))
+        l = l * np.exp(m - m_new) + float(np.exp(blk - m_new).sum())
+        m = m_new
+        trace.append((m, l))
+    p = np.exp(x - m) / l
+    return p, trace
+
+
+def flash_attention2_tiled(q, k, v, scale, causal, Br, Bc):
+    """FlashAttention-2 forward for one head in float64, block by block.
+
+    q: [Lq, d]; k, v: [Lk, d].  Returns (o [Lq, d], lse [Lq]).
+
+    Steps, in the order the pages give them:
+      outer loop over Q blocks of Br rows; state m = -inf, l = 0, O~ = 0;
+      inner loop over K/V blocks of Bc rows, ascending, skipping blocks whose
+      every key is masked for every row of the Q block (causal);
+        S = scale * Q_i K_j^T, masked keys set to -inf;
+        m' = max(m, rowmax S);  P~ = exp(S - m');  alpha = exp(m - m');
+        l = alpha * l + rowsum P~;  O~ = diag(alpha) O~ + P~ V_j;  m = m';
+      after the last block: O = O~ / l and lse = m + log(l).
+    "FlashAttention 怎么做? online softmax 怎么更新?" sections "推导 / 关键公式" and
+    "FlashAttention-2 改了什么"; "FlashAttention-2 算法架构升级" sections 一.2 (deferred
+    division) and 二.2 (Q loop outside); "Triton内核实战" section "流式注意力核心内核".
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Lq, d = q.shape
+    Lk = k.shape[0]
+    o = np.empty((Lq, d))
+    lse = np.empty(Lq)
+    for i0 in range(0, Lq, Br):
+        i1 = min(i0 + Br, Lq)
+        Qi = q[i0:i1]
+        rows = np.arange(i0, i1)
+        m = np.full(i1 - i0, -np.inf)
+        l = np.zeros(i1 - i0)
+        Ot = np.zeros((i1 - i0, d))
+        for j0 in range(0, Lk, Bc):
+            if causal and j0 > i1 - 1:
+                break                       # every later block is fully masked
+            j1 = min(j0 + Bc, Lk)
+            S = scale * (Qi @ k[j0:j1].T)
+            if causal:
+                cols = np.arange(j0, j1)
+                S = np.where(cols[None, :] > rows[:, None], -np.inf, S)
+            m_new = np.maximum(m, S.max(axis=1))
+            P = np.exp(S - m_new[:, None])
+            alpha = np.exp(m - m_new)
+            l = alpha * l + P.sum(axis=1)
+            Ot = alpha[:, None] * Ot + P @ v[j0:j1]
+            m = m_new
+        o[i0:i1] = Ot / l[:, None]
+        lse[i0:i1] = m + np.log(l)
+    return o, lse
