@@ -1,0 +1,90 @@
+"""ctypes binding of libfa2.so -- argument marshalling only.
+
+Every step of the forward pass runs in the HIP library.  There is no fallback:
+if libfa2.so is missing or fails to load, every entry point raises.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa2.so")
+
+FA2_OK = 0
+STATUS_NAMES = {
+    0: "FA2_OK", 1: "FA2_ERR_NULL", 2: "FA2_ERR_DIM", 3: "FA2_ERR_UNSUPPORTED_D",
+    4: "FA2_ERR_ARG", 5: "FA2_ERR_ALIGN", 6: "FA2_ERR_DEVICE", 7: "FA2_ERR_LAUNCH",
+}
+
+# name -> (restype, argtypes), exactly the declarations of include/fa2.h
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+SIGNATURES = {
+    "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa2_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa2_status_string": (ctypes.c_char_p, [_I]),
+    "fa2_check_args": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
+}
+
+_lib = None
+
+
+class FA2Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, status_string(status), STATUS_NAMES.get(status, status)))
+
+
+def lib():
+    """The loaded libfa2.so.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libfa2.so is not built (%s); build it with "
+                "`python -m flashattention_forward_fwd_amd.build` or __graft_entry__.build()" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status):
+    return lib().fa2_status_string(int(status)).decode()
+
+
+def _ptr(x):
+    """Device address of a tensor (data_ptr) or a raw integer address."""
+    if x is None:
+        return None
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return int(x)
+
+
+def fa2_fwd(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
+    """libfa2 ``fa2_fwd`` (bf16).  Tensors or raw device addresses; raises FA2Error."""
+    st = lib().fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                       int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                       _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_fwd")
+
+
+def fa2_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
+    """libfa2 ``fa2_fwd_f32``.  Tensors or raw device addresses; raises FA2Error."""
+    st = lib().fa2_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                           int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                           _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_fwd_f32")
+
+
+def fa2_check_args(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes):
+    """libfa2 ``fa2_check_args``: the status the entry points would return (no HIP call)."""
+    return lib().fa2_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                int(B), int(H), int(Lq), int(Lk), int(d), float(scale),
+                                int(causal), int(elem_bytes))

@@ -1,0 +1,84 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/fa2.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_forward_fwd_amd as fa
+from flashattention_forward_fwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa2.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa2_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert header_functions() == sorted(["fa2_fwd", "fa2_fwd_f32", "fa2_status_string", "fa2_check_args"])
+
+
+def test_library_exports_every_declared_symbol():
+    handle = ctypes.CDLL(_lib.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(handle, name), name
+    assert set(header_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings():
+    for code in range(8):
+        assert fa.status_string(code)
+    assert fa.status_string(99) == "unknown status"
+
+
+A = 1 << 20   # a 16-byte-aligned fake address (never dereferenced: checks run first)
+
+
+@pytest.mark.parametrize("elem", [2, 4])
+def test_argument_checks(elem):
+    ok = dict(q=A, k=A, v=A, o=A, lse=A, B=2, H=3, Lq=100, Lk=77, d=128, scale=0.1, causal=1)
+
+    def st(**kw):
+        a = dict(ok, **kw)
+        return fa.fa2_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"],
+                                 a["Lk"], a["d"], a["scale"], a["causal"], elem)
+    assert st() == 0
+    assert st(d=64) == 0
+    assert st(q=0) == 1 and st(lse=0) == 1 and st(v=0) == 1
+    assert st(B=0) == 2 and st(H=-1) == 2 and st(Lq=0) == 2 and st(Lk=0) == 2
+    assert st(B=1 << 30, H=1 << 30) == 2
+    for d in (0, 32, 96, 256, 127):
+        assert st(d=d) == 3
+    assert st(causal=2) == 4 and st(causal=-1) == 4
+    assert st(scale=0.0) == 4 and st(scale=-1.0) == 4
+    assert st(scale=float("inf")) == 4 and st(scale=float("nan")) == 4
+    assert st(q=A + 2) == 5 and st(o=A + 8) == 5 and st(lse=A + 4) == 5
+
+
+def test_entry_points_reject_before_touching_the_device():
+    """fa2_fwd / fa2_fwd_f32 return the validation status without any HIP call."""
+    L = fa.lib()
+    for fn in (L.fa2_fwd, L.fa2_fwd_f32):
+        assert fn(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, None) == 1
+        assert fn(A, A, A, A, A, 1, 1, 8, 8, 80, 0.1, 0, None) == 3
+        assert fn(A, A, A, A, A, 1, 0, 8, 8, 64, 0.1, 0, None) == 2
+        assert fn(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 3, None) == 4
+        assert fn(A, A + 6, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, None) == 5
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(fa.FA2Error) as e:
+        fa.fa2_fwd(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 0, None)
+    assert e.value.status == 3
+
+
+def test_forward_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q)

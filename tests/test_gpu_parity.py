@@ -1,0 +1,148 @@
+"""Parity of the HIP forward pass (through the C ABI) with the float64 oracle.
+
+Bars: bf16 inputs -- max|O - O_ref| <= 2e-2 and max|LSE - LSE_ref| <= 1e-3;
+fp32 inputs -- both <= 1e-5.  O_ref and LSE_ref are the oracle's unrounded
+float64 results on the exact (widened) inputs the device sees.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import flashattention_forward_fwd_amd as fa
+from flashattention_forward_fwd_amd.inputs import (WORKLOADS, head_row_samples, random_qkv,
+                                                   workload_inputs)
+from oracle import ref
+from tests.parity import TOL, check_case, compare, run_gpu, say, widen
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------ worked row (pages)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_worked_row_through_kernel(dtype):
+    """The pages' worked row (1,3 | 2,5): q = e0, K[:,0] = (1,3,2,5), V[:, :4] = I, scale 1.
+
+    Exact in bf16 and fp32; exercises the key-tail mask (4 valid keys of a 64-key tile).
+    """
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    d = 64
+    q = torch.zeros(1, 1, 1, d, dtype=tdt); q[0, 0, 0, 0] = 1
+    k = torch.zeros(1, 1, 4, d, dtype=tdt); k[0, 0, :, 0] = torch.tensor([1, 3, 2, 5], dtype=tdt)
+    v = torch.zeros(1, 1, 4, d, dtype=tdt); v[0, 0, :, :4] = torch.eye(4, dtype=tdt)
+    o, lse = run_gpu(q, k, v, False, 1.0)
+    x = np.array([1.0, 3.0, 2.0, 5.0])
+    p = np.exp(x - 5) / np.exp(x - 5).sum()
+    tol = TOL[dtype]
+    assert np.max(np.abs(o[0, 0, 0, :4] - p)) <= tol["o"]
+    assert np.all(o[0, 0, 0, 4:] == 0)
+    assert abs(lse[0, 0, 0] - (5 + math.log(1.2034379904932109))) <= tol["lse"]
+    assert abs(lse[0, 0, 0] - (5 + math.log(1.203))) <= 1e-3   # the page's printed l
+
+
+# --------------------------------------------- small and ragged shapes, full check
+SHAPES = [
+    # B, H, Lq,  Lk,  d
+    (1, 1, 1, 1, 64),
+    (1, 2, 2, 2, 128),
+    (1, 1, 1, 300, 64),
+    (1, 1, 300, 1, 128),
+    (2, 3, 129, 129, 64),
+    (1, 2, 257, 255, 128),
+    (1, 1, 64, 64, 128),
+    (1, 1, 65, 63, 64),
+    (2, 1, 127, 1000, 128),
+    (1, 2, 1000, 77, 128),
+    (1, 1, 384, 384, 64),
+    (1, 1, 500, 500, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_parity_ragged(shape, causal, dtype):
+    B, H, Lq, Lk, d = shape
+    q, k, v = random_qkv(B, H, Lq, Lk, d, dtype, seed=sum(shape) + 7 * causal)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(d)))
+    check_case("ragged %s %s" % (shape, dtype), q, k, v, causal, scale, dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_parity_large_score_range(causal):
+    """Q x 4 (as the ragged workload): peaky rows and frequent max rescaling."""
+    q, k, v = random_qkv(2, 2, 700, 900, 128, "bf16", seed=99, q_mult=4.0)
+    check_case("peaky", q, k, v, causal, float(np.float32(1 / np.sqrt(128))), "bf16")
+
+
+# ------------------------------------------------------------ the five workloads
+def _rows_for(name, w):
+    if name == "single_head_L256_d64_fp32" or name == "B3_H8_Lq1000_Lk7777_d128_bf16_q4":
+        return None                                   # every row
+    if name == "B1_H16_L16384_d128_bf16_causal":
+        return head_row_samples(w, 2048)              # 2048 seeded rows per head
+    return head_row_samples(w, 384)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_parity_workload(name):
+    w = WORKLOADS[name]
+    q, k, v = workload_inputs(w)
+    check_case(name, q, k, v, w.causal, w.scale, w.dtype, rows=_rows_for(name, w))
+
+
+# ----------------------------------------------------------- closed forms, edges
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_closed_forms(dtype):
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    B, H, L, d = 1, 2, 200, 128
+    _, _, v = random_qkv(B, H, L, L, d, dtype, seed=3)
+    q, _, _ = random_qkv(B, H, L, L, d, dtype, seed=4)
+    zeros = torch.zeros(B, H, L, d, dtype=tdt)
+    for causal in (False, True):
+        o, lse = run_gpu(q, zeros, v, causal, 0.125)
+        vv = widen(v)
+        n = np.arange(1, L + 1) if causal else np.full(L, L)
+        mean = np.cumsum(vv, axis=2) / n[None, None, :, None] if causal else np.broadcast_to(vv.mean(axis=2, keepdims=True), vv.shape)
+        assert np.max(np.abs(o - mean)) <= TOL[dtype]["o"]
+        assert np.max(np.abs(lse - np.log(n)[None, None])) <= TOL[dtype]["lse"]
+    const = torch.full((B, H, L, d), -1.75, dtype=tdt)
+    k = random_qkv(B, H, L, L, d, dtype, seed=5)[1]
+    o, _ = run_gpu(q, k, const, False, 0.125)
+    assert np.max(np.abs(o + 1.75)) <= TOL[dtype]["o"]
+    o, lse = run_gpu(q, k, v, True, 0.125)       # causal row 0 sees key 0 only
+    assert np.max(np.abs(o[:, :, 0] - widen(v)[:, :, 0])) <= TOL[dtype]["o"]
+    want = 0.125 * np.einsum("bhd,bhd->bh", widen(q)[:, :, 0], widen(k)[:, :, 0])
+    assert np.max(np.abs(lse[:, :, 0] - want)) <= TOL[dtype]["lse"]
+
+
+def test_bitwise_repeatable():
+    q, k, v = (t.cuda() for t in random_qkv(1, 4, 1500, 1500, 128, "bf16", seed=8))
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    o2, l2 = fa.forward(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_error_paths_on_device():
+    q = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FA2Error) as e:
+        fa.forward(q, q, q)
+    assert e.value.status == 3
+    buf = torch.zeros(1 + 1 * 1 * 8 * 64, dtype=torch.bfloat16, device="cuda")
+    mis = buf[1:].view(1, 1, 8, 64)               # 2-byte offset: misaligned
+    good = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(fa.FA2Error) as e:
+        fa.forward(mis, good, good)
+    assert e.value.status == 5
+
+
+def test_output_rows_all_written():
+    """Ragged Lq: every row of o and lse is overwritten (buffers start as NaN)."""
+    q, k, v = (t.cuda() for t in random_qkv(1, 3, 333, 129, 64, "bf16", seed=9))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 3, 333), float("nan"), device="cuda")
+    fa.forward(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
