@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention-2 forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one fa2_fwd call over the whole batch of the workload (inputs already
+resident in device memory).  Prints ONE JSON line with the throughput in
+attention-forward TFLOP/s (4*B*H*Lq*Lk*d, halved for causal), the roofline
+position of the kernel (HIP events on the launch stream), the HBM traffic taken
+from rocprofv3 counters (profiles/), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS (4·B·H·Lq·Lk·d) bf16 at N=2K–16K; % of MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X fp32, published
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_bf16_B2_H32_L4096_d128_causal_traffic.md")
+CONTEXT = {
+    "a100_fp16_tensor_tflops": 312, "a100_hbm_gbs": 1555, "a100_sram_tbs": 19,
+    "claimed_matmul_utilisation_fa1_to_fa2": "30-50% -> >70%",
+    "note": "figures quoted by the pages for NVIDIA A100; context only, not a target",
+}
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources, to tell whether stored counters are stale."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "flashattention_forward_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing, covers another workload, or predates the kernel."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+    if fields.get("workload") != workload_name:
+        return None
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, q, k, v, rows_per_head):
+    """The oracle, as it stands, on a seeded sample of query rows of every head."""
+    import numpy as np
+    import torch
+    from flashattention_forward_fwd_amd.inputs import head_row_samples
+    from oracle import ref
+
+    rows = head_row_samples(w, rows_per_head)
+    qd, kd, vd = (t.to(torch.float64).numpy() for t in (q, k, v))
+    threads = ref.default_threads()
+    ref.attention_f64(qd[:, :1], kd[:, :1], vd[:, :1], w.scale, w.causal, rows=rows[:1, :8], nthreads=threads)
+    t0 = time.perf_counter()
+    ref.attention_f64(qd, kd, vd, w.scale, w.causal, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    vis = np.minimum(rows + 1, w.Lk) if w.causal else np.full(rows.shape, w.Lk)
+    flops = float(4.0 * w.d * vis.sum())
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": "%d seeded query rows of each of the %d (batch, head) pairs (%.1f%% of rows), "
+                  "each against all its visible keys; %.3g FLOP in %.2f s, fp64"
+                  % (rows.shape[1], w.B * w.H, 100.0 * rows.shape[1] / w.Lq, flops, dt),
+    }
+
+
+def calibrate_copy(nbytes):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline causal N=4096, d=128)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="omit the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=0,
+                    help="query rows per (batch, head) for the oracle timing (0: every row)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the forward pass shards by (batch, head) and query tile with no exchange; "
+              "no multi-GPU run is part of it)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    import torch
+    import flashattention_forward_fwd_amd as fa
+    from flashattention_forward_fwd_amd.inputs import HEADLINE, WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.lib()   # fail loudly if the HIP library is missing
+    w = WORKLOADS[args.workload or HEADLINE]
+    q, k, v = workload_inputs(w)
+    dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = fa.fa2_fwd if w.dtype == "bf16" else fa.fa2_fwd_f32
+    call = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal), stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        fn(*call)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        fn(*call)
+        ev[i][1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / K
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_launch_ms = sum(launch_ms) / K
+
+    flops = w.flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    traffic = stored_traffic(w.name)
+    algo_bytes = (2 if w.dtype == "bf16" else 4) * w.B * w.H * (2 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
+                   "causal": w.causal, "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes,
+                   "wall_s_timed_region": round(wall, 4), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "avg_launch_ms": round(avg_launch_ms, 5),
+                     "min_launch_ms": round(min(launch_ms), 5)},
+        "context_pages": CONTEXT,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_rows_per_head if args.cpu_rows_per_head > 0 else w.Lq
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(n, w.Lq))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -43,6 +43,14 @@ def _lib():
     return _LIB
 
 
+def default_threads():
+    """OpenMP threads for the oracle: OMP_NUM_THREADS if set, else the usable cores."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
 def attention_f64(q, k, v, scale, causal, rows=None, nthreads=None):
     """Exact attention in float64 by its definition.
 
@@ -75,7 +83,7 @@ def attention_f64(q, k, v, scale, causal, rows=None, nthreads=None):
     o = np.empty((B, H, nr, d), dtype=np.float64)
     lse = np.empty((B, H, nr), dtype=np.float64)
     if nthreads is None:
-        nthreads = len(os.sched_getaffinity(0))
+        nthreads = default_threads()
     rc = _lib().oracle_attention_f64(
         q.ctypes.data, k.ctypes.data, v.ctypes.data,
         B, H, Lq, Lk, d, float(scale), int(bool(causal)),
