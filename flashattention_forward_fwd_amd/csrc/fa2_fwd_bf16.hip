@@ -18,15 +18,20 @@
 // "推导 / 关键公式", with the division deferred to the end as in
 // "FlashAttention-2 算法架构升级" section 一.2.
 //
-// Layout choices (MI355X-specific):
+// MI355X-specific choices:
+//  * K and V tiles go from HBM straight into LDS with asynchronous 16-byte
+//    global_load_lds transfers (no register staging), double-buffered: the
+//    transfer of tile j+1 runs while tile j is computed, one barrier per tile.
+//    Each 1 KiB transfer lands contiguously, so bank spreading is done by an XOR
+//    swizzle of the 16-byte chunks within a row, chosen at load time.
 //  * Scores are computed transposed (keys down the MFMA rows, queries across the
 //    lanes).  A lane then holds 16 keys of ONE query per 32x32 accumulator, so
 //    the row max / row sum need one exchange between the two wavefront halves,
 //    alpha is per lane, and the accumulator is already the B operand of the
-//    P~V product (up to a fixed permutation of keys that V^T in LDS absorbs).
-//  * K is kept row-major in LDS (the A operand reads 8 consecutive d).
-//    V is transposed into LDS with keys in that permuted order, so the A operand
-//    of the P~V product is one 16-byte read.
+//    P~V product.
+//  * V stays row-major in LDS; the A operand of the P~V product (8 keys of one
+//    d column per lane) is read with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16), two reads of 4 keys each.
 //  * Q stays in registers for the whole K/V loop (read from HBM once).
 #include "fa2_internal.h"
 
@@ -35,92 +40,68 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// LDS row pitches (elements).  The extra 8 elements (16 bytes) shift successive
-// rows across banks.
-template <int D> struct Lds {
-    static constexpr int kPitch = D + 8;         // K tile, row-major [key][d]
-    static constexpr int vPitch = kBc + 8;       // V tile, transposed [d][key']
+#define LDS_AS __attribute__((address_space(3)))
+
+template <int D> struct Tile {
+    static constexpr int kRowBytes = 2 * D;                  // one K or V row, bf16
+    static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
+    static constexpr int kRowsPerXfer = 1024 / kRowBytes;    // rows per 1 KiB wave transfer
+    static constexpr int kXfersPerWave = kBc * kRowBytes / 1024 / kWaves;
+    static constexpr int kElems = kBc * D;                   // elements per tile
+    static_assert(kXfersPerWave * kWaves * 1024 == kBc * kRowBytes, "tile must split into 1 KiB transfers");
+
+    // K: chunk q of row r is stored at chunk q ^ swz_k(r).  The score MFMA reads
+    // the same logical chunk from 32 consecutive rows; this spreads any 256
+    // consecutive bytes of those reads over all 64 banks.
+    static __device__ __forceinline__ int swz_k(int r)
+    {
+        return D == 128 ? (r & 15) : ((r >> 1) & 7);
+    }
+    // V: the transposing read takes 64 consecutive bytes (4 chunks) from each of
+    // 4 consecutive rows; moving each row's 4-chunk group to a different
+    // 64-byte bank group keeps those 4 rows conflict-free.
+    static __device__ __forceinline__ int swz_v(int r)
+    {
+        return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+    }
 };
 
-// Position of key `kk` (0..63 within a tile) in the transposed V tile.
-// Accumulator entry i of the 32x32 score tile t, in lane half h, is key
-// 32t + 8(i/4) + 4h + i%4.  The P~V MFMA over 16 keys (chunk c) takes 8 of
-// these per lane: entries 8(c%2)..8(c%2)+7 of tile c/2.  Storing key kk at
-// 16c + 8h + 4(a%2) + b  (a = (kk%32)/8, b = kk%4) makes those 8 keys one
-// contiguous 16-byte run at column 16c + 8h.
-__device__ __forceinline__ int vt_pos_of_group(int kg)   // kg = kk / 4
+// Issue this wavefront's share of the asynchronous HBM -> LDS copy of one K or V
+// tile (kBc rows from `k0`).  Rows past Lk are clamped to row Lk-1: their keys
+// are masked to -inf and their probabilities are exactly 0.
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile_async(const uint16_t *__restrict__ src, int k0, int Lk,
+                                                uint16_t *tile, int wave, int lane)
 {
-    const int t = kg >> 3, a = (kg >> 1) & 3, h = kg & 1;
-    const int c = 2 * t + (a >> 1);
-    return 16 * c + 8 * h + 4 * (a & 1);
-}
-
-template <int D>
-__device__ __forceinline__ void stage_kv_tile(const uint16_t *__restrict__ K,
-                                              const uint16_t *__restrict__ V,
-                                              int k0, int Lk, int tid,
-                                              uint16_t *sK, uint16_t *sVt)
-{
-    constexpr int KP = Lds<D>::kPitch, VP = Lds<D>::vPitch;
-    constexpr int kChunksPerRow = D / 8;                     // 16-byte chunks
-    // K: row-major copy, 16 bytes per access, consecutive threads along a row.
+    using T = Tile<D>;
 #pragma unroll
-    for (int r = 0; r < kBc * kChunksPerRow / kThreads; ++r) {
-        const int c = tid + kThreads * r;
-        const int row = c / kChunksPerRow;
-        const int col = (c % kChunksPerRow) * 8;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (k0 + row < Lk)
-            val = *reinterpret_cast<const u32x4 *>(K + (size_t)(k0 + row) * D + col);
-        *reinterpret_cast<u32x4 *>(sK + row * KP + col) = val;
-    }
-    // V: each thread takes 4 consecutive keys x 8 consecutive d and writes the
-    // 8 transposed runs of 4 keys (8 bytes each).
-    constexpr int kGroups = (kBc / 4) * kChunksPerRow;
-#pragma unroll
-    for (int g0 = 0; g0 < kGroups; g0 += kThreads) {
-        const int g = g0 + tid;
-        if (kGroups % kThreads != 0 && g >= kGroups) break;
-        const int dc = g % kChunksPerRow;
-        const int kg = g / kChunksPerRow;
-        u32x4 rows[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int key = k0 + 4 * kg + b;
-            rows[b] = u32x4{0u, 0u, 0u, 0u};
-            if (key < Lk)
-                rows[b] = *reinterpret_cast<const u32x4 *>(V + (size_t)key * D + dc * 8);
-        }
-        const int pos = vt_pos_of_group(kg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t r0 = rows[0][e], r1 = rows[1][e], r2 = rows[2][e], r3 = rows[3][e];
-            // element 2e of each row is the low half, element 2e+1 the high half
-            const u32x2 lo = {__builtin_amdgcn_perm(r1, r0, 0x05040100u),
-                              __builtin_amdgcn_perm(r3, r2, 0x05040100u)};
-            const u32x2 hi = {__builtin_amdgcn_perm(r1, r0, 0x07060302u),
-                              __builtin_amdgcn_perm(r3, r2, 0x07060302u)};
-            *reinterpret_cast<u32x2 *>(sVt + (8 * dc + 2 * e) * VP + pos) = lo;
-            *reinterpret_cast<u32x2 *>(sVt + (8 * dc + 2 * e + 1) * VP + pos) = hi;
-        }
+    for (int x = 0; x < T::kXfersPerWave; ++x) {
+        const int blk = wave * T::kXfersPerWave + x;             // 1 KiB block of the tile
+        const int row = blk * T::kRowsPerXfer + lane / T::kChunks;
+        const int phys = lane % T::kChunks;                      // where this lane's 16 B land
+        const int logical = phys ^ (IS_V ? T::swz_v(row) : T::swz_k(row));
+        int grow = k0 + row;
+        grow = grow < Lk ? grow : Lk - 1;
+        const uint16_t *g = src + (size_t)grow * D + logical * 8;
+        __builtin_amdgcn_global_load_lds(g, (LDS_AS void *)(tile + blk * 512), 16, 0, 0);
     }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
 {
-    constexpr int KP = Lds<D>::kPitch, VP = Lds<D>::vPitch;
+    using T = Tile<D>;
     constexpr int kDc = D / 16;          // 16-wide d chunks of the QK^T product
     constexpr int kDt = D / 32;          // 32-row d tiles of the output
-    __shared__ __attribute__((aligned(16))) uint16_t sK[kBc * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VP];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][T::kElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][T::kElems];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -139,6 +120,11 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     const int qrow = q0 + l32;                        // this lane's query row
     const bool wave_active = q0 < p.Lq;               // wave-uniform
     const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
+    const int n_kv = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
+
+    // first K/V tile in flight while Q is fetched
+    load_tile_async<D, false>(K, 0, p.Lk, sK[0], wave, lane);
+    load_tile_async<D, true>(V, 0, p.Lk, sV[0], wave, lane);
 
     // Q fragment: lane holds Q[qrow][16c + 8hh .. +7] for every chunk c.
     bf16x8 qf[kDc];
@@ -150,6 +136,16 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         qf[c] = __builtin_bit_cast(bf16x8, raw);
     }
 
+    // Per-lane LDS byte offsets.
+    // K (score A operand): row 32t + l32, logical chunk 2c + hh.  Because 2c and
+    // hh occupy different bits, chunk (2c + hh) ^ s == 2c ^ (hh ^ s).
+    const int k_lane = l32 * T::kRowBytes + 16 * (hh ^ T::swz_k(l32));
+    // V (transposing read): lane = 16g + 4e + r supplies row 4(g/2) + e (plus the
+    // chunk/read offset), columns 16(g%2) + 4r of d tile dt.
+    const int vg = lane >> 4, ve = (lane >> 2) & 3, vr = lane & 3;
+    const int v_row = 4 * (vg >> 1) + ve;
+    const int v_lane = v_row * T::kRowBytes + 64 * (T::swz_v(v_row) >> 2) + 32 * (vg & 1) + 8 * vr;
+
     f32x16 acc_o[kDt];
 #pragma unroll
     for (int t = 0; t < kDt; ++t)
@@ -158,86 +154,102 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     float lpart = 0.f;       // running sum over this lane's half of the keys
 
     const float c2 = p.scale_log2;
-    const int n_kv = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
     for (int j = 0; j < n_kv; ++j) {
+        const int cur = j & 1;
         const int k0 = j * kBc;
-        __syncthreads();                       // everyone is done with the previous tile
-        stage_kv_tile<D>(K, V, k0, p.Lk, tid, sK, sVt);
-        __syncthreads();
-
-        if (!wave_active) continue;
-        if (CAUSAL && k0 > wave_qlast) continue;   // every key is masked for this wave
-
-        // S^T (two 32x32 tiles of keys x queries)
-        f32x16 s[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            s[t] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < kDc; ++c) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sK + (32 * t + l32) * KP + 16 * c + 8 * hh);
-                s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[t], 0, 0, 0);
-            }
+        if (j + 1 < n_kv) {                   // next tile into the other buffer
+            load_tile_async<D, false>(K, k0 + kBc, p.Lk, sK[cur ^ 1], wave, lane);
+            load_tile_async<D, true>(V, k0 + kBc, p.Lk, sV[cur ^ 1], wave, lane);
         }
 
-        const bool need_mask = (k0 + kBc > p.Lk) || (CAUSAL && k0 + kBc - 1 > q0);
-        if (need_mask) {
+        if (wave_active && !(CAUSAL && k0 > wave_qlast)) {
+            const LDS_AS char *kb = (const LDS_AS char *)sK[cur];
+            const LDS_AS char *vb = (const LDS_AS char *)sV[cur];
+
+            // S^T (two 32x32 tiles of keys x queries)
+            f32x16 s[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                s[t] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < kDc; ++c) {
+                    const int off = (32 * t * T::kRowBytes + k_lane) ^ (32 * c);
+                    const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8 *>(kb + off);
+                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[t], 0, 0, 0);
+                }
+            }
+
+            const bool need_mask = (k0 + kBc > p.Lk) || (CAUSAL && k0 + kBc - 1 > q0);
+            if (need_mask) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = k0 + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
+                        const bool hidden = key >= p.Lk || (CAUSAL && key > qrow);
+                        s[t][i] = hidden ? -INFINITY : s[t][i];
+                    }
+            }
+
+            // running max over the row (this lane's 32 keys, then the other half's)
+            float mx = s[0][0];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, s[t][i]);
+            mx = fmaxf(mx, swap_halves(mx));
+            const float m_new = fmaxf(m, mx * c2);
+            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+
+            float rs = 0.f;
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int key = k0 + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
-                    const bool hidden = key >= p.Lk || (CAUSAL && key > qrow);
-                    s[t][i] = hidden ? -INFINITY : s[t][i];
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -m_new));
+                    s[t][i] = e;
+                    rs += e;
+                }
+            lpart = __builtin_fmaf(lpart, alpha, rs);
+            m = m_new;
+
+#pragma unroll
+            for (int t = 0; t < kDt; ++t)
+                acc_o[t] *= alpha;
+
+            // P~^T as bf16 B operands, one per 16-key chunk: slots 0-3 are keys
+            // 16c + 4hh + 0..3, slots 4-7 keys 16c + 8 + 4hh + 0..3.
+            bf16x8 pf[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int t = c >> 1, i0 = 8 * (c & 1);
+                const f32x8 v8 = {s[t][i0 + 0], s[t][i0 + 1], s[t][i0 + 2], s[t][i0 + 3],
+                                  s[t][i0 + 4], s[t][i0 + 5], s[t][i0 + 6], s[t][i0 + 7]};
+                pf[c] = __builtin_convertvector(v8, bf16x8);
+            }
+
+            // O~^T += V^T P~^T; the A operand of chunk c is two transposing reads
+            // (keys 16c + 4hh + 0..3 and 16c + 8 + 4hh + 0..3).
+#pragma unroll
+            for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int off0 = (16 * c * T::kRowBytes + v_lane) ^ (64 * dt);
+                    const int off1 = off0 + 8 * T::kRowBytes;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off0));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off1));
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], acc_o[dt], 0, 0, 0);
                 }
         }
 
-        // running max over the row (this lane's 32 keys, then the other half's)
-        float mx = s[0][0];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, s[t][i]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m, mx * c2);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-
-        float rs = 0.f;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -m_new));
-                s[t][i] = e;
-                rs += e;
-            }
-        lpart = __builtin_fmaf(lpart, alpha, rs);
-        m = m_new;
-
-#pragma unroll
-        for (int t = 0; t < kDt; ++t)
-            acc_o[t] *= alpha;
-
-        // P~^T as bf16 B operands, one per 16-key chunk
-        bf16x8 pf[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int t = c >> 1, i0 = 8 * (c & 1);
-            const f32x8 v8 = {s[t][i0 + 0], s[t][i0 + 1], s[t][i0 + 2], s[t][i0 + 3],
-                              s[t][i0 + 4], s[t][i0 + 5], s[t][i0 + 6], s[t][i0 + 7]};
-            pf[c] = __builtin_convertvector(v8, bf16x8);
-        }
-
-        // O~^T += V^T P~^T
-#pragma unroll
-        for (int dt = 0; dt < kDt; ++dt)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sVt + (32 * dt + l32) * VP + 16 * c + 8 * hh);
-                acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], acc_o[dt], 0, 0, 0);
-            }
+        __builtin_amdgcn_s_waitcnt(0);        // this wave's part of tile j+1 has landed
+        __syncthreads();                      // ... everyone's has, and tile j is no longer read
     }
 
     if (!wave_active) return;
