@@ -93,6 +93,118 @@ __device__ __forceinline__ void load_tile_async(const uint16_t *__restrict__ src
     }
 }
 
+// Threshold (base-2 units) for moving the running max.  While a row's max has
+// not grown by more than this, the old reference max is kept: P~ = 2^(S c - m)
+// is then at most 2^8, l and O~ keep the same reference, and nothing is
+// rescaled.  O = O~ / l and LSE = m + log2 l are unchanged by the choice of m.
+constexpr float kRescaleThreshold = 8.0f;
+
+// S^T = K_j Q_i^T for one wavefront: two 32x32 tiles of (keys x queries).
+template <int D>
+__device__ __forceinline__ void scores(const LDS_AS char *kb, const bf16x8 (&qf)[D / 16],
+                                       f32x16 (&s)[2], int k_lane)
+{
+    using T = Tile<D>;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            const int off = (32 * t * T::kRowBytes + k_lane) ^ (32 * c);
+            const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8 *>(kb + off);
+            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[t], 0, 0, 0);
+        }
+    }
+}
+
+// Keys past Lk, and (causal) keys after the lane's query, get -inf.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int k0, int Lk, int qrow, int hh)
+{
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
+            const bool hidden = key >= Lk || (CAUSAL && key > qrow);
+            s[t][i] = hidden ? -INFINITY : s[t][i];
+        }
+}
+
+// Row max (base-2 units) of a score tile: this lane's 32 keys, then the other half's.
+__device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[2], float c2)
+{
+    float mx = s[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            mx = fmaxf(mx, s[t][i]);
+    mx = fmaxf(mx, swap_halves(mx));
+    return mx * c2;
+}
+
+// Moves the reference max when some row of the wavefront grew past the
+// threshold; returns the factor O~ and l must be multiplied by (1: no move).
+__device__ __forceinline__ float update_max(float &m, float m_tile)
+{
+    const float m_cand = fmaxf(m, m_tile);
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(m_cand - m > kRescaleThreshold) != 0) {
+        alpha = __builtin_amdgcn_exp2f(m - m_cand);
+        m = m_cand;
+    }
+    return alpha;
+}
+
+// P~ = 2^(S c - m) as bf16 B operands (one per 16-key chunk: slots 0-3 are keys
+// 16c + 4hh + 0..3, slots 4-7 keys 16c + 8 + 4hh + 0..3), and its row sum.
+__device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, float m, bf16x8 (&pf)[4])
+{
+    float rs = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int t = c >> 1, i0 = 8 * (c & 1);
+        f32x8 v8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            v8[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i0 + e], c2, -m));
+            rs += v8[e];
+        }
+        pf[c] = __builtin_convertvector(v8, bf16x8);
+    }
+    return rs;
+}
+
+// O~^T += V_j^T P~^T; the A operand of chunk c is two transposing reads
+// (keys 16c + 4hh + 0..3 and 16c + 8 + 4hh + 0..3).
+template <int D>
+__device__ __forceinline__ void accumulate_pv(const LDS_AS char *vb, const bf16x8 (&pf)[4],
+                                              f32x16 (&acc_o)[D / 32], int v_lane)
+{
+    using T = Tile<D>;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int off0 = (16 * c * T::kRowBytes + v_lane) ^ (64 * dt);
+            const int off1 = off0 + 8 * T::kRowBytes;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off1));
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], acc_o[dt], 0, 0, 0);
+        }
+}
+
+template <int D>
+__device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, float alpha)
+{
+    lpart *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+        acc_o[t] *= alpha;
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
@@ -119,12 +231,25 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     const int q0 = qt * kBr + wave * kRowsPerWave;    // first row of this wavefront
     const int qrow = q0 + l32;                        // this lane's query row
     const bool wave_active = q0 < p.Lq;               // wave-uniform
-    const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
     const int n_kv = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
 
-    // first K/V tile in flight while Q is fetched
+    // Tiles this wavefront computes: [0, n_plain) need no mask, [n_plain, n_wave)
+    // cross the causal diagonal or the end of the keys; the work-group's other
+    // tiles are masked for all of its rows (it only helps load them).
+    int n_wave = 0, n_plain = 0;
+    if (wave_active) {
+        const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
+        n_wave = CAUSAL ? min(n_kv, wave_qlast / kBc + 1) : n_kv;
+        n_plain = min(n_wave, p.Lk / kBc);
+        if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / kBc);
+    }
+
+    // Tile t of K lives in sK[t % 2], of V in sV[t % 2].  Iteration j reads K_{j+1}
+    // (next scores) and V_j, and loads K_{j+2} and V_{j+1}.
     load_tile_async<D, false>(K, 0, p.Lk, sK[0], wave, lane);
     load_tile_async<D, true>(V, 0, p.Lk, sV[0], wave, lane);
+    if (n_kv > 1)
+        load_tile_async<D, false>(K, kBc, p.Lk, sK[1], wave, lane);
 
     // Q fragment: lane holds Q[qrow][16c + 8hh .. +7] for every chunk c.
     bf16x8 qf[kDc];
@@ -150,106 +275,65 @@ void fa2_fwd_bf16_kernel(FwdParams p)
 #pragma unroll
     for (int t = 0; t < kDt; ++t)
         acc_o[t] = f32x16{};
-    float m = -INFINITY;     // running max (base-2 units), per query row
+    float m = -INFINITY;     // reference max (base-2 units), per query row
     float lpart = 0.f;       // running sum over this lane's half of the keys
-
+    float alpha = 1.f;       // pending rescale of O~ and l
     const float c2 = p.scale_log2;
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int j = 0; j < n_kv; ++j) {
+    // Scores of the first tile.  Its max becomes the reference (O~ and l are 0).
+    f32x16 s_cur[2];
+    if (n_wave > 0) {
+        scores<D>((const LDS_AS char *)sK[0], qf, s_cur, k_lane);
+        if (n_plain == 0) mask_scores<CAUSAL>(s_cur, 0, p.Lk, qrow, hh);
+        m = row_max_scaled(s_cur, c2);
+    }
+    __syncthreads();                          // sK[0] may now be refilled
+
+    // Every wavefront passes the same n_kv barriers.
+    int j = 0;
+    for (; j + 1 < n_wave; ++j) {
         const int cur = j & 1;
-        const int k0 = j * kBc;
-        if (j + 1 < n_kv) {                   // next tile into the other buffer
-            load_tile_async<D, false>(K, k0 + kBc, p.Lk, sK[cur ^ 1], wave, lane);
-            load_tile_async<D, true>(V, k0 + kBc, p.Lk, sV[cur ^ 1], wave, lane);
-        }
+        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK[cur], wave, lane);
+        load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV[cur ^ 1], wave, lane);
+        if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
 
-        if (wave_active && !(CAUSAL && k0 > wave_qlast)) {
-            const LDS_AS char *kb = (const LDS_AS char *)sK[cur];
-            const LDS_AS char *vb = (const LDS_AS char *)sV[cur];
+        // VALU: probabilities of tile j;  MFMA: scores of tile j+1.
+        bf16x8 pf[4];
+        lpart += probabilities(s_cur, c2, m, pf);
+        f32x16 s_next[2];
+        scores<D>((const LDS_AS char *)sK[cur ^ 1], qf, s_next, k_lane);
 
-            // S^T (two 32x32 tiles of keys x queries)
-            f32x16 s[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                s[t] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < kDc; ++c) {
-                    const int off = (32 * t * T::kRowBytes + k_lane) ^ (32 * c);
-                    const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8 *>(kb + off);
-                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[t], 0, 0, 0);
-                }
-            }
+        // MFMA: O~ += P~_j V_j;  VALU: max of tile j+1.
+        accumulate_pv<D>((const LDS_AS char *)sV[cur], pf, acc_o, v_lane);
+        if (j + 1 >= n_plain) mask_scores<CAUSAL>(s_next, (j + 1) * kBc, p.Lk, qrow, hh);
+        alpha = update_max(m, row_max_scaled(s_next, c2));
+        s_cur[0] = s_next[0];
+        s_cur[1] = s_next[1];
 
-            const bool need_mask = (k0 + kBc > p.Lk) || (CAUSAL && k0 + kBc - 1 > q0);
-            if (need_mask) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = k0 + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
-                        const bool hidden = key >= p.Lk || (CAUSAL && key > qrow);
-                        s[t][i] = hidden ? -INFINITY : s[t][i];
-                    }
-            }
-
-            // running max over the row (this lane's 32 keys, then the other half's)
-            float mx = s[0][0];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, s[t][i]);
-            mx = fmaxf(mx, swap_halves(mx));
-            const float m_new = fmaxf(m, mx * c2);
-            const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-
-            float rs = 0.f;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -m_new));
-                    s[t][i] = e;
-                    rs += e;
-                }
-            lpart = __builtin_fmaf(lpart, alpha, rs);
-            m = m_new;
-
-#pragma unroll
-            for (int t = 0; t < kDt; ++t)
-                acc_o[t] *= alpha;
-
-            // P~^T as bf16 B operands, one per 16-key chunk: slots 0-3 are keys
-            // 16c + 4hh + 0..3, slots 4-7 keys 16c + 8 + 4hh + 0..3.
-            bf16x8 pf[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int t = c >> 1, i0 = 8 * (c & 1);
-                const f32x8 v8 = {s[t][i0 + 0], s[t][i0 + 1], s[t][i0 + 2], s[t][i0 + 3],
-                                  s[t][i0 + 4], s[t][i0 + 5], s[t][i0 + 6], s[t][i0 + 7]};
-                pf[c] = __builtin_convertvector(v8, bf16x8);
-            }
-
-            // O~^T += V^T P~^T; the A operand of chunk c is two transposing reads
-            // (keys 16c + 4hh + 0..3 and 16c + 8 + 4hh + 0..3).
-#pragma unroll
-            for (int dt = 0; dt < kDt; ++dt)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int off0 = (16 * c * T::kRowBytes + v_lane) ^ (64 * dt);
-                    const int off1 = off0 + 8 * T::kRowBytes;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off0));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off1));
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], acc_o[dt], 0, 0, 0);
-                }
-        }
-
-        __builtin_amdgcn_s_waitcnt(0);        // this wave's part of tile j+1 has landed
-        __syncthreads();                      // ... everyone's has, and tile j is no longer read
+        __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
+        __syncthreads();                      // ... everyone's, and the read buffers are free
+    }
+    if (j < n_wave) {                         // last computed tile: no next scores
+        const int cur = j & 1;
+        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK[cur], wave, lane);
+        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV[cur ^ 1], wave, lane);
+        if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
+        bf16x8 pf[4];
+        lpart += probabilities(s_cur, c2, m, pf);
+        accumulate_pv<D>((const LDS_AS char *)sV[cur], pf, acc_o, v_lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        ++j;
+    }
+    for (; j < n_kv; ++j) {                   // this wave only helps load
+        const int cur = j & 1;
+        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK[cur], wave, lane);
+        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV[cur ^ 1], wave, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
     }
 
     if (!wave_active) return;
