@@ -205,6 +205,28 @@ __device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, f
         acc_o[t] *= alpha;
 }
 
+// One step of the pipelined loop for tile j: probabilities of tile j (VALU)
+// while the scores of tile j+1 run (MFMA), then O~ += P~_j V_j (MFMA) while the
+// max of tile j+1 is taken (VALU).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const LDS_AS char *v_cur,
+                                               const bf16x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
+                                               f32x16 (&s_cur)[2], float &m, float &lpart, float &alpha,
+                                               float c2, int j, int n_plain, int Lk, int qrow, int hh,
+                                               int k_lane, int v_lane)
+{
+    if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
+    bf16x8 pf[4];
+    lpart += probabilities(s_cur, c2, m, pf);
+    f32x16 s_next[2];
+    scores<D>(k_next, qf, s_next, k_lane);
+    accumulate_pv<D>(v_cur, pf, acc_o, v_lane);
+    if (j + 1 >= n_plain) mask_scores<CAUSAL>(s_next, (j + 1) * kBc, Lk, qrow, hh);
+    alpha = update_max(m, row_max_scaled(s_next, c2));
+    s_cur[0] = s_next[0];
+    s_cur[1] = s_next[1];
+}
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
@@ -212,8 +234,14 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     using T = Tile<D>;
     constexpr int kDc = D / 16;          // 16-wide d chunks of the QK^T product
     constexpr int kDt = D / 32;          // 32-row d tiles of the output
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][T::kElems];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][T::kElems];
+    // Tile t of K lives in sK0 / sK1 by the parity of t, same for V.  Four
+    // separate variables (not one array) let the compiler see that reading one
+    // buffer does not depend on a transfer into another, so it does not wait
+    // for the transfers in flight before every LDS read.
+    __shared__ __attribute__((aligned(1024))) uint16_t sK0[T::kElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK1[T::kElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV0[T::kElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV1[T::kElems];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -246,10 +274,10 @@ void fa2_fwd_bf16_kernel(FwdParams p)
 
     // Tile t of K lives in sK[t % 2], of V in sV[t % 2].  Iteration j reads K_{j+1}
     // (next scores) and V_j, and loads K_{j+2} and V_{j+1}.
-    load_tile_async<D, false>(K, 0, p.Lk, sK[0], wave, lane);
-    load_tile_async<D, true>(V, 0, p.Lk, sV[0], wave, lane);
+    load_tile_async<D, false>(K, 0, p.Lk, sK0, wave, lane);
+    load_tile_async<D, true>(V, 0, p.Lk, sV0, wave, lane);
     if (n_kv > 1)
-        load_tile_async<D, false>(K, kBc, p.Lk, sK[1], wave, lane);
+        load_tile_async<D, false>(K, kBc, p.Lk, sK1, wave, lane);
 
     // Q fragment: lane holds Q[qrow][16c + 8hh .. +7] for every chunk c.
     bf16x8 qf[kDc];
@@ -286,52 +314,49 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     // Scores of the first tile.  Its max becomes the reference (O~ and l are 0).
     f32x16 s_cur[2];
     if (n_wave > 0) {
-        scores<D>((const LDS_AS char *)sK[0], qf, s_cur, k_lane);
+        scores<D>((const LDS_AS char *)sK0, qf, s_cur, k_lane);
         if (n_plain == 0) mask_scores<CAUSAL>(s_cur, 0, p.Lk, qrow, hh);
         m = row_max_scaled(s_cur, c2);
     }
-    __syncthreads();                          // sK[0] may now be refilled
+    __syncthreads();                          // sK0 may now be refilled
 
-    // Every wavefront passes the same n_kv barriers.
+    // Every wavefront passes the same n_kv barriers.  The pipelined loop is
+    // unrolled over two tiles so each buffer is fixed at compile time.
     int j = 0;
-    for (; j + 1 < n_wave; ++j) {
-        const int cur = j & 1;
-        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK[cur], wave, lane);
-        load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV[cur ^ 1], wave, lane);
-        if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
-
-        // VALU: probabilities of tile j;  MFMA: scores of tile j+1.
-        bf16x8 pf[4];
-        lpart += probabilities(s_cur, c2, m, pf);
-        f32x16 s_next[2];
-        scores<D>((const LDS_AS char *)sK[cur ^ 1], qf, s_next, k_lane);
-
-        // MFMA: O~ += P~_j V_j;  VALU: max of tile j+1.
-        accumulate_pv<D>((const LDS_AS char *)sV[cur], pf, acc_o, v_lane);
-        if (j + 1 >= n_plain) mask_scores<CAUSAL>(s_next, (j + 1) * kBc, p.Lk, qrow, hh);
-        alpha = update_max(m, row_max_scaled(s_next, c2));
-        s_cur[0] = s_next[0];
-        s_cur[1] = s_next[1];
-
+    while (j + 1 < n_wave) {
+        // even tile j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1
+        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK0, wave, lane);
+        load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV1, wave, lane);
+        pipelined_step<D, CAUSAL>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur,
+                                  m, lpart, alpha, c2, j, n_plain, p.Lk, qrow, hh, k_lane, v_lane);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
         __syncthreads();                      // ... everyone's, and the read buffers are free
+        if (++j + 1 >= n_wave) break;
+        // odd tile j: K_{j+1} in sK0, V_j in sV1; loads K_{j+2} -> sK1, V_{j+1} -> sV0
+        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK1, wave, lane);
+        load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV0, wave, lane);
+        pipelined_step<D, CAUSAL>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur,
+                                  m, lpart, alpha, c2, j, n_plain, p.Lk, qrow, hh, k_lane, v_lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        ++j;
     }
     if (j < n_wave) {                         // last computed tile: no next scores
-        const int cur = j & 1;
-        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK[cur], wave, lane);
-        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV[cur ^ 1], wave, lane);
+        const bool odd = j & 1;
+        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, odd ? sK1 : sK0, wave, lane);
+        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, odd ? sV0 : sV1, wave, lane);
         if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
         bf16x8 pf[4];
         lpart += probabilities(s_cur, c2, m, pf);
-        accumulate_pv<D>((const LDS_AS char *)sV[cur], pf, acc_o, v_lane);
+        accumulate_pv<D>((const LDS_AS char *)(odd ? sV1 : sV0), pf, acc_o, v_lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         ++j;
     }
     for (; j < n_kv; ++j) {                   // this wave only helps load
-        const int cur = j & 1;
-        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK[cur], wave, lane);
-        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV[cur ^ 1], wave, lane);
+        const bool odd = j & 1;
+        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, odd ? sK1 : sK0, wave, lane);
+        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, odd ? sV0 : sV1, wave, lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
