@@ -26,26 +26,22 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kRowsPerWave = 32;   // query rows owned by one wavefront (one 32-wide MFMA tile)
 constexpr int kBr = kWaves * kRowsPerWave;   // query rows per work-group
 constexpr int kBc = 64;            // keys per K/V tile
-constexpr int kXcds = 8;           // accelerator complex dies on MI355X
 constexpr float kLn2 = 0.693147180559945309417f;
 
 // Work-group id -> (batch*head, query tile).
 //
-// The dispatcher hands consecutive work-group ids to the XCDs in turn, and each
-// XCD has its own L2.  Remapping so that the ids an XCD receives are consecutive
-// in the logical order keeps the query tiles of one (batch, head) -- which read
-// the same K and V -- on one XCD.  Within a (batch, head) the tiles run from the
-// last to the first: under the causal mask the last query tile has the most key
-// tiles, so the long work-groups start first and the short ones fill the tail.
+// Query tiles run from the last to the first across all heads (heads are the
+// fast index): under the causal mask the last query tile has the most key
+// tiles, so the long work-groups start first and the short ones fill the tail
+// (longest-processing-time-first).  The dispatcher hands consecutive
+// work-group ids to the eight XCDs in turn, so with this order each XCD serves
+// a fixed subset of heads, and its resident work-groups walk the same K/V
+// tiles of those heads at about the same pace, which keeps them in its L2.
 __device__ __forceinline__ void map_workgroup(int w, int n_wg, int n_qtiles, int &bh, int &qt)
 {
-    const int xcd = w % kXcds;
-    const int slot = w / kXcds;
-    const int per = n_wg / kXcds;
-    const int rem = n_wg % kXcds;
-    const int logical = xcd * per + (xcd < rem ? xcd : rem) + slot;
-    bh = logical / n_qtiles;
-    qt = n_qtiles - 1 - (logical - bh * n_qtiles);
+    const int n_bh = n_wg / n_qtiles;
+    qt = n_qtiles - 1 - w / n_bh;
+    bh = w % n_bh;
 }
 
 // Number of K/V tiles a query tile visits.  Causal: only tiles holding a key
