@@ -20,10 +20,14 @@
 //
 // MI355X-specific choices:
 //  * K and V tiles go from HBM straight into LDS with asynchronous 16-byte
-//    global_load_lds transfers (no register staging), double-buffered: the
-//    transfer of tile j+1 runs while tile j is computed, one barrier per tile.
+//    buffer loads (LDS DMA, no register staging), double-buffered, one barrier
+//    per tile; rows past Lk lie outside the buffer range and arrive as zeros.
 //    Each 1 KiB transfer lands contiguously, so bank spreading is done by an XOR
 //    swizzle of the 16-byte chunks within a row, chosen at load time.
+//  * Software pipelining inside the wavefront: the exponentials of tile j run
+//    on the VALU while the MFMA unit computes the scores of tile j+1, and the
+//    max of tile j+1 is taken while the P~V product of tile j runs.  K is
+//    loaded two tiles ahead, V one.
 //  * Scores are computed transposed (keys down the MFMA rows, queries across the
 //    lanes).  A lane then holds 16 keys of ONE query per 32x32 accumulator, so
 //    the row max / row sum need one exchange between the two wavefront halves,
@@ -53,6 +57,9 @@ template <int D> struct Tile {
     static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
     static constexpr int kRowsPerXfer = 1024 / kRowBytes;    // rows per 1 KiB wave transfer
     static constexpr int kXfersPerWave = kBc * kRowBytes / 1024 / kWaves;
+    static constexpr int kBytes = kBc * kRowBytes;
+    // K swizzle repeats every kKPeriod transfers (see swz_k).
+    static constexpr int kKPeriod = D == 128 ? 4 : 2;
     static constexpr int kElems = kBc * D;                   // elements per tile
     static_assert(kXfersPerWave * kWaves * 1024 == kBc * kRowBytes, "tile must split into 1 KiB transfers");
 
@@ -72,24 +79,49 @@ template <int D> struct Tile {
     }
 };
 
-// Issue this wavefront's share of the asynchronous HBM -> LDS copy of one K or V
-// tile (kBc rows from `k0`).  Rows past Lk are clamped to row Lk-1: their keys
-// are masked to -inf and their probabilities are exactly 0.
+// Buffer-resource word 3 for raw (unswizzled, unformatted) buffer access on gfx9.
+constexpr int kRawBufferFlags = 0x00020000;
+
+// Per-lane byte offsets of the tile loads.  Transfer x of wavefront w moves
+// 1 KiB block b = w * kXfersPerWave + x of the tile; lane l lands at byte 16 l
+// of the block, i.e. row b * kRowsPerXfer + l / kChunks, physical chunk
+// l % kChunks, and reads that row's logical chunk.  The K swizzle depends on
+// b % kKPeriod, the V swizzle only on the lane.
+template <int D> struct LoadOffsets {
+    int k[Tile<D>::kKPeriod];
+    int v;
+};
+
+template <int D>
+__device__ __forceinline__ LoadOffsets<D> load_offsets(int lane)
+{
+    using T = Tile<D>;
+    LoadOffsets<D> o;
+    const int phys = lane % T::kChunks;
+#pragma unroll
+    for (int b = 0; b < T::kKPeriod; ++b) {
+        const int row = b * T::kRowsPerXfer + lane / T::kChunks;
+        o.k[b] = row * T::kRowBytes + 16 * (phys ^ T::swz_k(row));
+    }
+    const int row = lane / T::kChunks;
+    o.v = row * T::kRowBytes + 16 * (phys ^ T::swz_v(row));
+    return o;
+}
+
+// Issue this wavefront's share of the asynchronous HBM -> LDS copy of tile
+// `tile` of K (IS_V false) or V.  Rows past Lk lie outside the buffer range
+// and arrive as zeros; their keys are masked to -inf.
 template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile_async(const uint16_t *__restrict__ src, int k0, int Lk,
-                                                uint16_t *tile, int wave, int lane)
+__device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t src, int tile, uint16_t *dst,
+                                                int wave, const LoadOffsets<D> &off)
 {
     using T = Tile<D>;
 #pragma unroll
     for (int x = 0; x < T::kXfersPerWave; ++x) {
-        const int blk = wave * T::kXfersPerWave + x;             // 1 KiB block of the tile
-        const int row = blk * T::kRowsPerXfer + lane / T::kChunks;
-        const int phys = lane % T::kChunks;                      // where this lane's 16 B land
-        const int logical = phys ^ (IS_V ? T::swz_v(row) : T::swz_k(row));
-        int grow = k0 + row;
-        grow = grow < Lk ? grow : Lk - 1;
-        const uint16_t *g = src + (size_t)grow * D + logical * 8;
-        __builtin_amdgcn_global_load_lds(g, (LDS_AS void *)(tile + blk * 512), 16, 0, 0);
+        const int b = wave * T::kXfersPerWave + x;
+        const int voff = IS_V ? off.v : off.k[x % T::kKPeriod];
+        const int soff = tile * T::kBytes + (IS_V ? b : b - b % T::kKPeriod) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void *)(dst + b * 512), 16, voff, soff, 0, 0);
     }
 }
 
@@ -253,8 +285,12 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     map_workgroup(blockIdx.x, p.n_wg, p.n_qtiles, bh, qt);
 
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + (size_t)bh * p.Lq * D;
-    const uint16_t *K = static_cast<const uint16_t *>(p.k) + (size_t)bh * p.Lk * D;
-    const uint16_t *V = static_cast<const uint16_t *>(p.v) + (size_t)bh * p.Lk * D;
+    const size_t kv_off = (size_t)bh * p.Lk * D;
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.k) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.v) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+    const LoadOffsets<D> loff = load_offsets<D>(lane);
 
     const int q0 = qt * kBr + wave * kRowsPerWave;    // first row of this wavefront
     const int qrow = q0 + l32;                        // this lane's query row
@@ -274,10 +310,10 @@ void fa2_fwd_bf16_kernel(FwdParams p)
 
     // Tile t of K lives in sK[t % 2], of V in sV[t % 2].  Iteration j reads K_{j+1}
     // (next scores) and V_j, and loads K_{j+2} and V_{j+1}.
-    load_tile_async<D, false>(K, 0, p.Lk, sK0, wave, lane);
-    load_tile_async<D, true>(V, 0, p.Lk, sV0, wave, lane);
+    load_tile_async<D, false>(rK, 0, sK0, wave, loff);
+    load_tile_async<D, true>(rV, 0, sV0, wave, loff);
     if (n_kv > 1)
-        load_tile_async<D, false>(K, kBc, p.Lk, sK1, wave, lane);
+        load_tile_async<D, false>(rK, 1, sK1, wave, loff);
 
     // Q fragment: lane holds Q[qrow][16c + 8hh .. +7] for every chunk c.
     bf16x8 qf[kDc];
@@ -325,16 +361,16 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     int j = 0;
     while (j + 1 < n_wave) {
         // even tile j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1
-        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK0, wave, lane);
-        load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV1, wave, lane);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, sK0, wave, loff);
+        load_tile_async<D, true>(rV, j + 1, sV1, wave, loff);
         pipelined_step<D, CAUSAL>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur,
                                   m, lpart, alpha, c2, j, n_plain, p.Lk, qrow, hh, k_lane, v_lane);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
         __syncthreads();                      // ... everyone's, and the read buffers are free
         if (++j + 1 >= n_wave) break;
         // odd tile j: K_{j+1} in sK0, V_j in sV1; loads K_{j+2} -> sK1, V_{j+1} -> sV0
-        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, sK1, wave, lane);
-        load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, sV0, wave, lane);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, sK1, wave, loff);
+        load_tile_async<D, true>(rV, j + 1, sV0, wave, loff);
         pipelined_step<D, CAUSAL>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur,
                                   m, lpart, alpha, c2, j, n_plain, p.Lk, qrow, hh, k_lane, v_lane);
         __builtin_amdgcn_s_waitcnt(0);
@@ -343,8 +379,8 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     }
     if (j < n_wave) {                         // last computed tile: no next scores
         const bool odd = j & 1;
-        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, odd ? sK1 : sK0, wave, lane);
-        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, odd ? sV0 : sV1, wave, lane);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, odd ? sK1 : sK0, wave, loff);
+        if (j + 1 < n_kv) load_tile_async<D, true>(rV, j + 1, odd ? sV0 : sV1, wave, loff);
         if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
         bf16x8 pf[4];
         lpart += probabilities(s_cur, c2, m, pf);
@@ -355,8 +391,8 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     }
     for (; j < n_kv; ++j) {                   // this wave only helps load
         const bool odd = j & 1;
-        if (j + 2 < n_kv) load_tile_async<D, false>(K, (j + 2) * kBc, p.Lk, odd ? sK1 : sK0, wave, lane);
-        if (j + 1 < n_kv) load_tile_async<D, true>(V, (j + 1) * kBc, p.Lk, odd ? sV0 : sV1, wave, lane);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, odd ? sK1 : sK0, wave, loff);
+        if (j + 1 < n_kv) load_tile_async<D, true>(rV, j + 1, odd ? sV0 : sV1, wave, loff);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }

@@ -35,8 +35,8 @@ constexpr float kLn2 = 0.693147180559945309417f;
 // tiles, so the long work-groups start first and the short ones fill the tail
 // (longest-processing-time-first).  The dispatcher hands consecutive
 // work-group ids to the eight XCDs in turn, so with this order each XCD serves
-// a fixed subset of heads, and its resident work-groups walk the same K/V
-// tiles of those heads at about the same pace, which keeps them in its L2.
+// a fixed subset of heads, and its resident work-groups walk the K/V tiles of
+// those heads at about the same pace.
 __device__ __forceinline__ void map_workgroup(int w, int n_wg, int n_qtiles, int &bh, int &qt)
 {
     const int n_bh = n_wg / n_qtiles;
