@@ -249,12 +249,22 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
 {
     if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
     bf16x8 pf[4];
-    lpart += probabilities(s_cur, c2, m, pf);
+    const float rs = probabilities(s_cur, c2, m, pf);
     f32x16 s_next[2];
     scores<D>(k_next, qf, s_next, k_lane);
     accumulate_pv<D>(v_cur, pf, acc_o, v_lane);
-    if (j + 1 >= n_plain) mask_scores<CAUSAL>(s_next, (j + 1) * kBc, Lk, qrow, hh);
-    alpha = update_max(m, row_max_scaled(s_next, c2));
+    float mt = row_max_scaled(s_next, c2);
+    // The row sum and the next max are consumed after the branch below; this
+    // use keeps their VALU work in this block, between the MFMAs, instead of
+    // letting it sink past the branch where nothing overlaps it.
+    asm volatile("" ::"v"(rs), "v"(mt));
+    lpart += rs;
+    // Tiles on the causal diagonal or the key tail (few): mask, take the max again.
+    if (j + 1 >= n_plain) {
+        mask_scores<CAUSAL>(s_next, (j + 1) * kBc, Lk, qrow, hh);
+        mt = row_max_scaled(s_next, c2);
+    }
+    alpha = update_max(m, mt);
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
 }
