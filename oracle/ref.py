@@ -15,6 +15,9 @@ Three references, each a plain reading of the pages:
   (Q blocks outside, K/V blocks inside, running m and l, unnormalised output, one
   division at the end, logsumexp), used to show on the CPU that the tiled method
   reaches the definition's result.
+* ``merge_partials`` -- the combine of attention results over disjoint key sets
+  from their outputs and logsumexps (ring attention's two-segment merge, and
+  FlashDecoding's reduce step).
 """
 import ctypes
 import os
@@ -180,4 +183,36 @@ def flash_attention2_tiled(q, k, v, scale, causal, Br, Bc):
             m = m_new
         o[i0:i1] = Ot / l[:, None]
         lse[i0:i1] = m + np.log(l)
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine attention results over disjoint key sets into the result over their union.
+
+    o_parts: [S, ..., d], each part's output normalised by its own row sum;
+    lse_parts: [S, ...], each part's logsumexp (natural log; -inf where the part
+    has no visible key, in which case its output is ignored and may hold anything).
+    Returns (o [..., d], lse [...]) in float64.
+
+    Two normalised segments merge as L = log(e^L1 + e^L2) and
+    O = e^(L1 - L) O1 + e^(L2 - L) O2 ("FlashAttention 怎么做? online softmax 怎么更新?",
+    follow-up "多卡(ring attention)怎么合并两段结果?").  More parts are folded in one
+    at a time with the same two-segment step, which is FlashDecoding's reduce over
+    its K/V splits ("Flash Attention 全解析（上）" section 4.3).  A row whose parts
+    are all empty gets O = 0 and L = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    o = np.zeros(o_parts.shape[1:])
+    lse = np.full(lse_parts.shape[1:], -np.inf)
+    for s in range(o_parts.shape[0]):
+        l2 = lse_parts[s]
+        o2 = np.where(np.isneginf(l2)[..., None], 0.0, o_parts[s])   # an empty part is not read
+        l_new = np.logaddexp(lse, l2)
+        seen = ~np.isneginf(l_new)
+        safe = np.where(seen, l_new, 0.0)
+        w1 = np.where(seen, np.exp(lse - safe), 0.0)
+        w2 = np.where(seen, np.exp(l2 - safe), 0.0)
+        o = w1[..., None] * o + w2[..., None] * o2
+        lse = l_new
     return o, lse

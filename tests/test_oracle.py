@@ -306,3 +306,113 @@ def test_planted_mistakes_are_caught(name, tmp_path):
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
     assert caught, "planted mistake %r passed every pin" % name
+
+
+# --------------------------------------------------------------- merge of partials
+# ref.merge_partials is pinned to the definition (attention over all keys, whose
+# oracle is pinned above), to scipy's logsumexp, and to closed forms.
+
+MERGE_BOUNDS = [(0, 37), (37, 38), (38, 160), (160, 300)]
+
+
+def _shard_inputs(seed=21):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((2, 3, 50, 64))
+    k = rng.standard_normal((2, 3, 300, 64))
+    v = rng.standard_normal((2, 3, 300, 64))
+    return q, k, v, 0.2
+
+
+def _shard_results(q, k, v, scale, bounds):
+    """Oracle attention of every query against each key shard [a, b), non-causal."""
+    parts = [ref.attention_f64(q, k[:, :, a:b], v[:, :, a:b], scale, False) for a, b in bounds]
+    return np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts])
+
+
+def merge_pin_definition(merge):
+    """Merging the results over key shards gives attention over all keys."""
+    q, k, v, scale = _shard_inputs()
+    o_parts, l_parts = _shard_results(q, k, v, scale, MERGE_BOUNDS)
+    o, lse = merge(o_parts, l_parts)
+    o_ref, l_ref = ref.attention_f64(q, k, v, scale, False)
+    assert np.max(np.abs(o - o_ref)) < 1e-12
+    assert np.max(np.abs(lse - l_ref)) < 1e-12
+
+
+def merge_pin_logsumexp(merge):
+    """LSE of the merge is scipy's logsumexp over the parts; O is a convex combination."""
+    rng = np.random.default_rng(5)
+    l_parts = rng.normal(0.0, 6.0, size=(5, 40))
+    o_parts = rng.standard_normal((5, 40, 8))
+    o, lse = merge(o_parts, l_parts)
+    assert np.max(np.abs(lse - logsumexp(l_parts, axis=0))) < 1e-12
+    w = softmax(l_parts, axis=0)
+    assert np.max(np.abs(o - np.einsum("sr,srd->rd", w, o_parts))) < 1e-12
+
+
+def merge_pin_closed_forms(merge):
+    """Equal halves: L + ln 2 and the mean; weights 3:1 at L = 1000 (no overflow)."""
+    o1 = np.array([[1.0, -2.0, 0.5]])
+    o2 = np.array([[3.0, 4.0, -0.5]])
+    o, lse = merge(np.stack([o1, o2]), np.array([[0.7], [0.7]]))
+    assert abs(lse[0] - (0.7 + math.log(2))) < 1e-14
+    assert np.max(np.abs(o - (o1 + o2) / 2)) < 1e-14
+    o, lse = merge(np.stack([o1, o2]), np.array([[1000.0], [1000.0 - math.log(3)]]))
+    assert abs(lse[0] - (1000.0 + math.log(4 / 3))) < 1e-11
+    assert np.max(np.abs(o - (0.75 * o1 + 0.25 * o2))) < 1e-13
+
+
+def merge_pin_empty_parts(merge):
+    """A -inf part is ignored (its O is not read); an all-empty row is O = 0, L = -inf."""
+    o1 = np.array([[1.0, 2.0], [5.0, 6.0]])
+    junk = np.full((2, 2), np.nan)
+    o, lse = merge(np.stack([junk, o1, junk]),
+                   np.array([[-np.inf, -np.inf], [0.25, -np.inf], [-np.inf, -np.inf]]))
+    assert np.array_equal(o[0], o1[0]) and lse[0] == 0.25
+    assert np.array_equal(o[1], [0.0, 0.0]) and lse[1] == -np.inf
+
+
+MERGE_PINS = [merge_pin_definition, merge_pin_logsumexp, merge_pin_closed_forms, merge_pin_empty_parts]
+
+
+@pytest.mark.parametrize("pin", MERGE_PINS, ids=lambda f: f.__name__)
+def test_merge_pin(pin):
+    pin(ref.merge_partials)
+
+
+def test_merge_order_invariant():
+    q, k, v, scale = _shard_inputs(seed=3)
+    o_parts, l_parts = _shard_results(q, k, v, scale, MERGE_BOUNDS)
+    perm = [2, 0, 3, 1]
+    o1, l1 = ref.merge_partials(o_parts, l_parts)
+    o2, l2 = ref.merge_partials(o_parts[perm], l_parts[perm])
+    assert np.max(np.abs(o1 - o2)) < 1e-13 and np.max(np.abs(l1 - l2)) < 1e-13
+
+
+# Plausible mistakes in the merge; each must fail at least one merge pin.
+MERGE_MUTANTS = {
+    "weight_without_max": ("np.exp(l2 - safe)", "np.exp(l2)"),
+    "max_instead_of_logsumexp": ("np.logaddexp(lse, l2)", "np.maximum(lse, l2)"),
+    "unweighted_sum": ("w1[..., None] * o + w2[..., None] * o2", "o + o2"),
+    "old_weight_from_new_part": ("np.exp(lse - safe)", "np.exp(l2 - safe)"),
+    "empty_part_read": ("np.where(np.isneginf(l2)[..., None], 0.0, o_parts[s])", "o_parts[s]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_MUTANTS))
+def test_merge_planted_mistakes_are_caught(name):
+    import inspect
+    import textwrap
+    old, new = MERGE_MUTANTS[name]
+    src = textwrap.dedent(inspect.getsource(ref.merge_partials))
+    assert src.count(old) == 1, old
+    ns = {"np": np}
+    exec(src.replace(old, new), ns)
+    caught = []
+    for pin in MERGE_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(ns["merge_partials"])
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, "planted mistake %r passed every merge pin" % name
