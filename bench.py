@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the FlashAttention-2 forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits S]
 
 A step is one fa2_fwd call over the whole batch of the workload (inputs already
-resident in device memory).  Prints ONE JSON line with the throughput in
+resident in device memory); with --splits, one fa2_fwd_splitkv call (partial
+kernel + merge kernel, workspace allocated before the timed region).  Prints ONE JSON line with the throughput in
 attention-forward TFLOP/s (4*B*H*Lq*Lk*d, halved for causal), the roofline
 position of the kernel (HIP events on the launch stream), the HBM traffic taken
 from rocprofv3 counters (profiles/), and the CPU oracle timed on a bounded
@@ -101,12 +102,17 @@ def calibrate_copy(nbytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The default warm-up (about 60 ms of kernels on the headline workload) lets
+    # the GPU clock settle: with 10 warm-up steps the first timed steps ran ~13 %
+    # slower on MI355X.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline causal N=4096, d=128)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="omit the oracle timing (profiling runs)")
     ap.add_argument("--cpu-rows-per-head", type=int, default=0,
                     help="query rows per (batch, head) for the oracle timing (0: every row)")
+    ap.add_argument("--splits", type=int, default=None, metavar="S",
+                    help="time the split-KV path with S K/V ranges (0: the library's choice)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -122,20 +128,34 @@ def main():
 
     import torch
     import flashattention_forward_fwd_amd as fa
-    from flashattention_forward_fwd_amd.inputs import HEADLINE, WORKLOADS, workload_inputs
+    from flashattention_forward_fwd_amd.inputs import DECODE_WORKLOADS, HEADLINE, WORKLOADS, workload_inputs
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.lib()   # fail loudly if the HIP library is missing
-    w = WORKLOADS[args.workload or HEADLINE]
+    w = dict(WORKLOADS, **DECODE_WORKLOADS)[args.workload or HEADLINE]
     q, k, v = workload_inputs(w)
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
     o = torch.empty_like(dq)
     lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    fn = fa.fa2_fwd if w.dtype == "bf16" else fa.fa2_fwd_f32
-    call = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal), stream.cuda_stream)
+    args_common = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal))
+    split_info = None
+    if args.splits is None:
+        fn = fa.fa2_fwd if w.dtype == "bf16" else fa.fa2_fwd_f32
+        call = args_common + (stream.cuda_stream,)
+    else:
+        if w.dtype != "bf16":
+            print("bench.py: the split-KV path takes bf16 workloads", file=sys.stderr)
+            sys.exit(2)
+        S = args.splits or fa.fa2_splitkv_num_splits(w.B, w.H, w.Lq, w.Lk, w.d, int(w.causal))
+        ws_bytes = fa.fa2_splitkv_workspace_bytes(w.B, w.H, w.Lq, w.Lk, w.d, int(w.causal), S)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        fn = fa.fa2_fwd_splitkv
+        call = args_common + (S, workspace, ws_bytes, stream.cuda_stream)
+        split_info = {"num_splits": S, "requested": args.splits, "workspace_bytes": ws_bytes,
+                      "timed_call": "fa2_fwd_splitkv = partial kernel + merge kernel"}
 
     for _ in range(args.warmup):
         fn(*call)
@@ -160,10 +180,19 @@ def main():
 
     flops = w.flops
     value = flops / (ms_step * 1e-3) / 1e12
-    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    traffic = stored_traffic(w.name)
+    traffic = stored_traffic(w.name) if split_info is None else None
     algo_bytes = (2 if w.dtype == "bf16" else 4) * w.B * w.H * (2 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq
+    # Bound by whichever roof is lower at this arithmetic intensity.
+    if flops / algo_bytes >= (peak * 1e12) / (PEAK_HBM_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(flops / (avg_launch_ms * 1e-3) / 1e12, 2), "peak": peak,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(algo_bytes / (avg_launch_ms * 1e-3) / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof.update({"traffic": traffic, "avg_launch_ms": round(avg_launch_ms, 5),
+                 "min_launch_ms": round(min(launch_ms), 5)})
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
@@ -173,12 +202,11 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
                    "causal": w.causal, "flops_per_step": flops, "algorithmic_bytes_per_step": algo_bytes,
                    "wall_s_timed_region": round(wall, 4), "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "avg_launch_ms": round(avg_launch_ms, 5),
-                     "min_launch_ms": round(min(launch_ms), 5)},
+        "roofline": roof,
         "context_pages": CONTEXT,
     }
+    if split_info is not None:
+        out["config"]["split_kv"] = split_info
     if not args.no_cpu_baseline:
         n = args.cpu_rows_per_head if args.cpu_rows_per_head > 0 else w.Lq
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(n, w.Lq))

@@ -9,17 +9,26 @@ and the stream.
 """
 import math
 
-from ._lib import FA2Error, fa2_check_args, fa2_fwd, fa2_fwd_f32, lib, status_string  # noqa: F401
+from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_check_args, fa2_fwd, fa2_fwd_f32,  # noqa: F401
+                   fa2_fwd_splitkv, fa2_merge_partials, fa2_splitkv_num_splits,
+                   fa2_splitkv_workspace_bytes, lib, status_string)
 
-__all__ = ["forward", "fa2_fwd", "fa2_fwd_f32", "fa2_check_args", "FA2Error", "status_string"]
+__all__ = ["forward", "merge_partials", "fa2_fwd", "fa2_fwd_f32", "fa2_fwd_splitkv",
+           "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
+           "fa2_check_args", "FA2Error", "status_string", "FA2_MAX_SPLITS"]
 
 
-def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, workspace=None):
     """O = softmax(scale * Q K^T [causal]) V and the per-row logsumexp.
 
     q: [B, H, Lq, d], k and v: [B, H, Lk, d], all bf16 or all fp32 CUDA tensors
     (made contiguous).  scale defaults to fp32(1/sqrt(d)).  Returns (o, lse)
     with o like q and lse fp32 [B, H, Lq].  Enqueued on the current stream.
+
+    num_splits (bf16 only): None runs the one-pass kernel; an int runs the
+    split-KV path with that many K/V ranges (0: the library picks).  Its
+    workspace is allocated here unless a large enough uint8 device tensor is
+    given.
     """
     import torch
 
@@ -41,6 +50,45 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None):
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    c = int(bool(causal))
+    if num_splits is not None:
+        if q.dtype != torch.bfloat16:
+            raise ValueError("the split-KV path takes bfloat16 tensors")
+        need = fa2_splitkv_workspace_bytes(B, H, Lq, Lk, d, c, num_splits)
+        if need == 0:
+            raise ValueError("sizes or num_splits rejected by fa2_splitkv_workspace_bytes")
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        fa2_fwd_splitkv(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, num_splits, workspace,
+                        workspace.numel() * workspace.element_size(), stream)
+        return out, lse
     fn = fa2_fwd if q.dtype == torch.bfloat16 else fa2_fwd_f32
-    fn(q, k, v, out, lse, B, H, Lq, Lk, d, scale, int(bool(causal)), stream)
+    fn(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, stream)
+    return out, lse
+
+
+def merge_partials(o_parts, lse_parts, out=None, lse=None):
+    """Combine partial results over disjoint key sets (libfa2 ``fa2_merge_partials``).
+
+    o_parts: fp32 [S, ..., d], lse_parts: fp32 [S, ...] (natural-log
+    logsumexps, -inf for an empty part) on the device.  Returns (o, lse) with
+    o bf16 [..., d] and lse fp32 [...].  Enqueued on the current stream.
+    """
+    import torch
+
+    if not (o_parts.is_cuda and lse_parts.is_cuda):
+        raise ValueError("o_parts and lse_parts must be device tensors (no CPU path)")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts and lse_parts must be float32")
+    if tuple(o_parts.shape[:-1]) != tuple(lse_parts.shape) or lse_parts.dim() < 2:
+        raise ValueError("o_parts must be lse_parts' shape plus a trailing d")
+    S, d = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
+    if out is None:
+        out = torch.empty(o_parts.shape[1:], dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device)
+    stream = torch.cuda.current_stream(o_parts.device).cuda_stream
+    fa2_merge_partials(o_parts, lse_parts, S, rows, d, out, lse, stream)
     return out, lse

@@ -13,17 +13,25 @@ FA2_OK = 0
 STATUS_NAMES = {
     0: "FA2_OK", 1: "FA2_ERR_NULL", 2: "FA2_ERR_DIM", 3: "FA2_ERR_UNSUPPORTED_D",
     4: "FA2_ERR_ARG", 5: "FA2_ERR_ALIGN", 6: "FA2_ERR_DEVICE", 7: "FA2_ERR_LAUNCH",
+    8: "FA2_ERR_WORKSPACE",
 }
+FA2_MAX_SPLITS = 128
 
 # name -> (restype, argtypes), exactly the declarations of include/fa2.h
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_Z = ctypes.c_size_t
+_L = ctypes.c_int64
 SIGNATURES = {
     "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa2_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa2_status_string": (ctypes.c_char_p, [_I]),
     "fa2_check_args": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
+    "fa2_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "fa2_splitkv_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "fa2_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
+    "fa2_merge_partials": (_I, [_P, _P, _I, _L, _I, _P, _P, _P]),
 }
 
 _lib = None
@@ -88,3 +96,32 @@ def fa2_check_args(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes):
     return lib().fa2_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                 int(B), int(H), int(Lq), int(Lk), int(d), float(scale),
                                 int(causal), int(elem_bytes))
+
+
+def fa2_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
+                    workspace_bytes, stream):
+    """libfa2 ``fa2_fwd_splitkv`` (bf16, split K/V + merge).  Raises FA2Error."""
+    st = lib().fa2_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                               int(num_splits), _ptr(workspace), int(workspace_bytes), _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_fwd_splitkv")
+
+
+def fa2_splitkv_workspace_bytes(B, H, Lq, Lk, d, causal, num_splits):
+    """libfa2 ``fa2_splitkv_workspace_bytes``: bytes of workspace (0: sizes rejected)."""
+    return lib().fa2_splitkv_workspace_bytes(int(B), int(H), int(Lq), int(Lk), int(d), int(causal),
+                                             int(num_splits))
+
+
+def fa2_splitkv_num_splits(B, H, Lq, Lk, d, causal):
+    """libfa2 ``fa2_splitkv_num_splits``: the split count that num_splits=0 selects."""
+    return lib().fa2_splitkv_num_splits(int(B), int(H), int(Lq), int(Lk), int(d), int(causal))
+
+
+def fa2_merge_partials(o_parts, lse_parts, n_parts, rows, d, o, lse, stream):
+    """libfa2 ``fa2_merge_partials``.  Raises FA2Error."""
+    st = lib().fa2_merge_partials(_ptr(o_parts), _ptr(lse_parts), int(n_parts), int(rows), int(d),
+                                  _ptr(o), _ptr(lse), _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_merge_partials")

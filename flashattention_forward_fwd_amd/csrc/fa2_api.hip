@@ -14,6 +14,13 @@ namespace {
 // Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_ok[kMaxDevices];
+std::atomic<int> g_device_cus[kMaxDevices];     // compute units, 0 = not queried yet
+
+// Work-groups of the forward kernels that one compute unit holds at once.
+constexpr int kWorkgroupsPerCU = 2;
+// Fewest K/V tiles a split-KV range should have, so the partial kernel's
+// software pipeline and double buffering have something to overlap.
+constexpr int kMinTilesPerSplit = 8;
 
 int check_device()
 {
@@ -32,6 +39,22 @@ int check_device()
     if (dev < kMaxDevices)
         g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
     return ok ? FA2_OK : FA2_ERR_DEVICE;
+}
+
+// Compute units of the current device (0 if it cannot be queried).
+int device_cus()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < kMaxDevices) {
+        const int known = g_device_cus[dev].load(std::memory_order_relaxed);
+        if (known > 0) return known;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 0;
+    if (dev < kMaxDevices) g_device_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -61,6 +84,9 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
         return FA2_ERR_ALIGN;
     const int64_t L = Lq > Lk ? Lq : Lk;
     if (!product_fits(B, H, L, (int64_t)d * elem_bytes)) return FA2_ERR_DIM;
+    // One head's K (or V), plus one tile, must stay below 2 GiB: tiles are
+    // addressed with 32-bit buffer offsets.
+    if (((int64_t)Lk + fa2::kBc) * d * elem_bytes > INT32_MAX) return FA2_ERR_DIM;
     const int64_t n_qtiles = (Lq + fa2::kBr - 1) / fa2::kBr;
     if ((int64_t)B * H > INT32_MAX / n_qtiles) return FA2_ERR_DIM;   // grid size
     if (out) {
@@ -69,9 +95,54 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
         out->B = B; out->H = H; out->Lq = Lq; out->Lk = Lk;
         out->scale_log2 = (float)((double)scale * 1.4426950408889634074);
         out->n_qtiles = (int)n_qtiles;
+        out->n_splits = 1;
         out->n_wg = (int)(n_qtiles * B * H);
     }
     return FA2_OK;
+}
+
+// Split count for num_splits == 0: the fewest ranges that put one work-group
+// on every compute unit, or two under the causal mask (query tiles then differ
+// in length, and finer pieces even out the end of the launch).  Measured on
+// MI355X, more splits than that cost more in partial-result traffic and per
+// work-group start-up than they gain.  Every range keeps at least
+// kMinTilesPerSplit K/V tiles.
+int auto_splits(int B, int H, int Lq, int Lk, int causal)
+{
+    const int cus = device_cus();
+    if (cus <= 0) return 1;
+    const int64_t target = (int64_t)cus * (causal ? kWorkgroupsPerCU : 1);
+    const int64_t n_qtiles = (Lq + fa2::kBr - 1) / fa2::kBr;
+    const int64_t base = n_qtiles * B * H;
+    if (base >= target) return 1;
+    // K/V tiles of the longest query tile (the last one).
+    const int tiles = fa2::kv_tiles_for((int)n_qtiles - 1, Lq, Lk, causal != 0);
+    int64_t S = (target + base - 1) / base;
+    if (S > tiles / kMinTilesPerSplit) S = tiles / kMinTilesPerSplit;
+    if (S > FA2_MAX_SPLITS) S = FA2_MAX_SPLITS;
+    return S < 1 ? 1 : (int)S;
+}
+
+// Byte size of the partial outputs [S, rows, d] fp32, rounded up so the
+// partial logsumexps that follow start on a 256-byte boundary.
+size_t partial_o_bytes(int64_t S, int64_t rows, int d)
+{
+    const size_t b = (size_t)S * rows * d * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+// The merge grid (d/4 threads per row, 256 per work-group) fits in a launch.
+bool merge_grid_fits(int64_t rows, int d)
+{
+    return rows <= (int64_t)INT32_MAX / (d / 4) * 256;
+}
+
+// Workspace size for S splits, 0 if it overflows.
+size_t workspace_bytes(int64_t S, int B, int H, int Lq, int d)
+{
+    const int64_t rows = (int64_t)B * H * Lq;
+    if (!product_fits(S, rows, d + 1, sizeof(float))) return 0;
+    return partial_o_bytes(S, rows, d) + (size_t)S * rows * sizeof(float);
 }
 
 }  // namespace
@@ -108,17 +179,91 @@ int fa2_fwd_f32(const float *q, const float *k, const float *v, float *o, float 
     return FA2_OK;
 }
 
+int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal)
+{
+    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || (d != 64 && d != 128)) return 1;
+    return auto_splits(B, H, Lq, Lk, causal);
+}
+
+size_t fa2_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int causal, int num_splits)
+{
+    // Size checks of fa2_fwd_splitkv, on stand-in aligned pointers.
+    const void *fake = reinterpret_cast<const void *>(uintptr_t(256));
+    if (prepare(fake, fake, fake, fake, static_cast<const float *>(fake), B, H, Lq, Lk, d, 1.0f,
+                causal, 2, nullptr) != FA2_OK)
+        return 0;
+    if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return 0;
+    const int S = num_splits == 0 ? auto_splits(B, H, Lq, Lk, causal) : num_splits;
+    return workspace_bytes(S, B, H, Lq, d);
+}
+
+int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                    int num_splits, void *workspace, size_t workspace_bytes_given, void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p);
+    if (st != FA2_OK) return st;
+    if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return FA2_ERR_ARG;
+    if (!workspace) return FA2_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA2_ERR_ALIGN;
+    if ((st = check_device()) != FA2_OK) return st;
+    const int S = num_splits == 0 ? auto_splits(B, H, Lq, Lk, causal) : num_splits;
+    if ((int64_t)p.n_wg * S > INT32_MAX) return FA2_ERR_DIM;
+    const int64_t rows = (int64_t)B * H * Lq;
+    if (!merge_grid_fits(rows, d)) return FA2_ERR_DIM;
+    const size_t need = workspace_bytes(S, B, H, Lq, d);
+    if (need == 0) return FA2_ERR_DIM;
+    if (workspace_bytes_given < need) return FA2_ERR_WORKSPACE;
+
+    float *o_parts = static_cast<float *>(workspace);
+    float *lse_parts = reinterpret_cast<float *>(static_cast<char *>(workspace) + partial_o_bytes(S, rows, d));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (S == 1) {                             // one range: the one-pass kernel
+        if (fa2::launch_fwd_bf16(p, d, causal != 0, s) != hipSuccess) return FA2_ERR_LAUNCH;
+        return FA2_OK;
+    }
+    fa2::FwdParams pp = p;
+    pp.o = o_parts;
+    pp.lse = lse_parts;
+    pp.n_splits = S;
+    pp.n_wg = p.n_wg * S;
+    if (fa2::launch_fwd_bf16_split(pp, d, causal != 0, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    if (fa2::launch_merge(o_parts, lse_parts, S, rows, d, o, lse, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
+                       int d, void *o, float *lse, void *stream)
+{
+    if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL;
+    if (n_parts < 1 || n_parts > FA2_MAX_SPLITS) return FA2_ERR_ARG;
+    if (rows < 1) return FA2_ERR_DIM;
+    if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_D;
+    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
+        return FA2_ERR_ALIGN;
+    if (!product_fits(n_parts, rows, d, sizeof(float))) return FA2_ERR_DIM;
+    if (!merge_grid_fits(rows, d)) return FA2_ERR_DIM;
+    int st = check_device();
+    if (st != FA2_OK) return st;
+    if (fa2::launch_merge(o_parts, lse_parts, n_parts, rows, d, o, lse, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
 const char *fa2_status_string(int status)
 {
     switch (status) {
     case FA2_OK: return "ok";
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
-    case FA2_ERR_DIM: return "B, H, Lq, Lk must be positive and the sizes must fit";
+    case FA2_ERR_DIM: return "B, H, Lq, Lk must be positive and the sizes must fit (one head's K below 2 GiB)";
     case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 64 or 128";
     case FA2_ERR_ARG: return "causal must be 0 or 1 and scale finite and positive";
     case FA2_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
+    case FA2_ERR_WORKSPACE: return "split-KV workspace missing or too small";
     default: return "unknown status";
     }
 }

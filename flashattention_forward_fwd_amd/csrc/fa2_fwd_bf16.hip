@@ -178,15 +178,28 @@ __device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[2], float c2)
 
 // Moves the reference max when some row of the wavefront grew past the
 // threshold; returns the factor O~ and l must be multiplied by (1: no move).
+// EMPTY_ROWS: a row may have seen no visible key yet (m = -inf; only in a
+// causal K/V range that starts after some of the wavefront's rows).  Such a
+// row keeps m = -inf and alpha = 1 until its first visible key arrives.
+template <bool EMPTY_ROWS>
 __device__ __forceinline__ float update_max(float &m, float m_tile)
 {
     const float m_cand = fmaxf(m, m_tile);
     float alpha = 1.0f;
     if (__builtin_amdgcn_ballot_w64(m_cand - m > kRescaleThreshold) != 0) {
         alpha = __builtin_amdgcn_exp2f(m - m_cand);
+        if (EMPTY_ROWS && m_cand == -INFINITY) alpha = 1.0f;
         m = m_cand;
     }
     return alpha;
+}
+
+// The max the probabilities are taken against: a row that has seen no visible
+// key (m = -inf, all its scores -inf) uses 0, so its probabilities are 0.
+template <bool EMPTY_ROWS>
+__device__ __forceinline__ float reference_max(float m)
+{
+    return (EMPTY_ROWS && m == -INFINITY) ? 0.0f : m;
 }
 
 // P~ = 2^(S c - m) as bf16 B operands (one per 16-key chunk: slots 0-3 are keys
@@ -240,16 +253,16 @@ __device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, f
 // One step of the pipelined loop for tile j: probabilities of tile j (VALU)
 // while the scores of tile j+1 run (MFMA), then O~ += P~_j V_j (MFMA) while the
 // max of tile j+1 is taken (VALU).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool EMPTY_ROWS>
 __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const LDS_AS char *v_cur,
                                                const bf16x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
                                                f32x16 (&s_cur)[2], float &m, float &lpart, float &alpha,
-                                               float c2, int j, int n_plain, int Lk, int qrow, int hh,
-                                               int k_lane, int v_lane)
+                                               float c2, int j, int t0, int n_plain, int Lk, int qrow,
+                                               int hh, int k_lane, int v_lane)
 {
     if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
     bf16x8 pf[4];
-    const float rs = probabilities(s_cur, c2, m, pf);
+    const float rs = probabilities(s_cur, c2, reference_max<EMPTY_ROWS>(m), pf);
     f32x16 s_next[2];
     scores<D>(k_next, qf, s_next, k_lane);
     accumulate_pv<D>(v_cur, pf, acc_o, v_lane);
@@ -261,19 +274,25 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
     lpart += rs;
     // Tiles on the causal diagonal or the key tail (few): mask, take the max again.
     if (j + 1 >= n_plain) {
-        mask_scores<CAUSAL>(s_next, (j + 1) * kBc, Lk, qrow, hh);
+        mask_scores<CAUSAL>(s_next, (t0 + j + 1) * kBc, Lk, qrow, hh);
         mt = row_max_scaled(s_next, c2);
     }
-    alpha = update_max(m, mt);
+    alpha = update_max<EMPTY_ROWS>(m, mt);
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
 }
 
-template <int D, bool CAUSAL>
+// SPLIT: the work-group covers one of p.n_splits contiguous ranges of its
+// query tile's K/V tiles and writes the fp32 partial O (normalised by its own
+// row sum) and partial LSE of that range; rows that see no key of the range
+// get LSE = -inf and no O.  Otherwise it covers all tiles and writes bf16 O.
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
 {
     using T = Tile<D>;
+    // Only a causal range that starts after tile 0 can hold rows without a visible key.
+    constexpr bool kEmptyRows = SPLIT && CAUSAL;
     constexpr int kDc = D / 16;          // 16-wide d chunks of the QK^T product
     constexpr int kDt = D / 32;          // 32-row d tiles of the output
     // Tile t of K lives in sK0 / sK1 by the parity of t, same for V.  Four
@@ -291,8 +310,24 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
-    int bh, qt;
-    map_workgroup(blockIdx.x, p.n_wg, p.n_qtiles, bh, qt);
+    int bh, qt, split = 0;
+    if (SPLIT) {
+        split = blockIdx.x % p.n_splits;
+        map_workgroup(blockIdx.x / p.n_splits, p.n_wg / p.n_splits, p.n_qtiles, bh, qt);
+    } else {
+        map_workgroup(blockIdx.x, p.n_wg, p.n_qtiles, bh, qt);
+    }
+    const int n_kv_all = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
+    // This work-group's K/V tiles: [t0, t0 + n_kv).
+    const int t0 = SPLIT ? (int)((int64_t)split * n_kv_all / p.n_splits) : 0;
+    const int n_kv = SPLIT ? (int)((int64_t)(split + 1) * n_kv_all / p.n_splits) - t0 : n_kv_all;
+    // Partial-result row of (split, bh, query 0 of this head).
+    const size_t part_row0 = ((size_t)split * p.B * p.H + bh) * p.Lq;
+    if (SPLIT && n_kv == 0) {                 // empty range: every row is empty
+        const int r = qt * kBr + tid;
+        if (tid < kBr && r < p.Lq) p.lse[part_row0 + r] = -INFINITY;
+        return;
+    }
 
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + (size_t)bh * p.Lq * D;
     const size_t kv_off = (size_t)bh * p.Lk * D;
@@ -305,25 +340,28 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     const int q0 = qt * kBr + wave * kRowsPerWave;    // first row of this wavefront
     const int qrow = q0 + l32;                        // this lane's query row
     const bool wave_active = q0 < p.Lq;               // wave-uniform
-    const int n_kv = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
 
-    // Tiles this wavefront computes: [0, n_plain) need no mask, [n_plain, n_wave)
-    // cross the causal diagonal or the end of the keys; the work-group's other
-    // tiles are masked for all of its rows (it only helps load them).
+    // Tiles this wavefront computes, counted from t0: [0, n_plain) need no mask,
+    // [n_plain, n_wave) cross the causal diagonal or the end of the keys; the
+    // work-group's other tiles are masked for all of its rows (it only helps
+    // load them).
     int n_wave = 0, n_plain = 0;
     if (wave_active) {
         const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
-        n_wave = CAUSAL ? min(n_kv, wave_qlast / kBc + 1) : n_kv;
-        n_plain = min(n_wave, p.Lk / kBc);
-        if (CAUSAL) n_plain = min(n_plain, (q0 + 1) / kBc);
+        const int end = CAUSAL ? min(t0 + n_kv, wave_qlast / kBc + 1) : t0 + n_kv;
+        int plain = min(end, p.Lk / kBc);
+        if (CAUSAL) plain = min(plain, (q0 + 1) / kBc);
+        n_wave = max(end - t0, 0);
+        n_plain = min(max(plain - t0, 0), n_wave);
     }
 
-    // Tile t of K lives in sK[t % 2], of V in sV[t % 2].  Iteration j reads K_{j+1}
-    // (next scores) and V_j, and loads K_{j+2} and V_{j+1}.
-    load_tile_async<D, false>(rK, 0, sK0, wave, loff);
-    load_tile_async<D, true>(rV, 0, sV0, wave, loff);
+    // Local tile j (global tile t0 + j) of K lives in sK[j % 2], of V in
+    // sV[j % 2].  Iteration j reads K_{j+1} (next scores) and V_j, and loads
+    // K_{j+2} and V_{j+1}.
+    load_tile_async<D, false>(rK, t0, sK0, wave, loff);
+    load_tile_async<D, true>(rV, t0, sV0, wave, loff);
     if (n_kv > 1)
-        load_tile_async<D, false>(rK, 1, sK1, wave, loff);
+        load_tile_async<D, false>(rK, t0 + 1, sK1, wave, loff);
 
     // Q fragment: lane holds Q[qrow][16c + 8hh .. +7] for every chunk c.
     bf16x8 qf[kDc];
@@ -361,7 +399,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     f32x16 s_cur[2];
     if (n_wave > 0) {
         scores<D>((const LDS_AS char *)sK0, qf, s_cur, k_lane);
-        if (n_plain == 0) mask_scores<CAUSAL>(s_cur, 0, p.Lk, qrow, hh);
+        if (n_plain == 0) mask_scores<CAUSAL>(s_cur, t0 * kBc, p.Lk, qrow, hh);
         m = row_max_scaled(s_cur, c2);
     }
     __syncthreads();                          // sK0 may now be refilled
@@ -371,29 +409,31 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     int j = 0;
     while (j + 1 < n_wave) {
         // even tile j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1
-        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, sK0, wave, loff);
-        load_tile_async<D, true>(rV, j + 1, sV1, wave, loff);
-        pipelined_step<D, CAUSAL>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur,
-                                  m, lpart, alpha, c2, j, n_plain, p.Lk, qrow, hh, k_lane, v_lane);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK0, wave, loff);
+        load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
+        pipelined_step<D, CAUSAL, kEmptyRows>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o,
+                                              s_cur, m, lpart, alpha, c2, j, t0, n_plain, p.Lk, qrow, hh,
+                                              k_lane, v_lane);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
         __syncthreads();                      // ... everyone's, and the read buffers are free
         if (++j + 1 >= n_wave) break;
         // odd tile j: K_{j+1} in sK0, V_j in sV1; loads K_{j+2} -> sK1, V_{j+1} -> sV0
-        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, sK1, wave, loff);
-        load_tile_async<D, true>(rV, j + 1, sV0, wave, loff);
-        pipelined_step<D, CAUSAL>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur,
-                                  m, lpart, alpha, c2, j, n_plain, p.Lk, qrow, hh, k_lane, v_lane);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK1, wave, loff);
+        load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
+        pipelined_step<D, CAUSAL, kEmptyRows>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o,
+                                              s_cur, m, lpart, alpha, c2, j, t0, n_plain, p.Lk, qrow, hh,
+                                              k_lane, v_lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         ++j;
     }
     if (j < n_wave) {                         // last computed tile: no next scores
         const bool odd = j & 1;
-        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, odd ? sK1 : sK0, wave, loff);
-        if (j + 1 < n_kv) load_tile_async<D, true>(rV, j + 1, odd ? sV0 : sV1, wave, loff);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, odd ? sK1 : sK0, wave, loff);
+        if (j + 1 < n_kv) load_tile_async<D, true>(rV, t0 + j + 1, odd ? sV0 : sV1, wave, loff);
         if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
         bf16x8 pf[4];
-        lpart += probabilities(s_cur, c2, m, pf);
+        lpart += probabilities(s_cur, c2, reference_max<kEmptyRows>(m), pf);
         accumulate_pv<D>((const LDS_AS char *)(odd ? sV1 : sV0), pf, acc_o, v_lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -401,8 +441,8 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     }
     for (; j < n_kv; ++j) {                   // this wave only helps load
         const bool odd = j & 1;
-        if (j + 2 < n_kv) load_tile_async<D, false>(rK, j + 2, odd ? sK1 : sK0, wave, loff);
-        if (j + 1 < n_kv) load_tile_async<D, true>(rV, j + 1, odd ? sV0 : sV1, wave, loff);
+        if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, odd ? sK1 : sK0, wave, loff);
+        if (j + 1 < n_kv) load_tile_async<D, true>(rV, t0 + j + 1, odd ? sV0 : sV1, wave, loff);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -410,6 +450,24 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     if (!wave_active) return;
     const float l = lpart + swap_halves(lpart);
     if (qrow >= p.Lq) return;
+    if (SPLIT) {
+        float lse = -INFINITY;
+        if (l > 0.0f) {                       // the row saw a key of this range
+            const float inv_l = 1.0f / l;
+            float *Op = static_cast<float *>(p.o) + (part_row0 + qrow) * D;
+#pragma unroll
+            for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 v4 = {acc_o[dt][4 * a + 0] * inv_l, acc_o[dt][4 * a + 1] * inv_l,
+                                      acc_o[dt][4 * a + 2] * inv_l, acc_o[dt][4 * a + 3] * inv_l};
+                    *reinterpret_cast<f32x4 *>(Op + 32 * dt + 8 * a + 4 * hh) = v4;
+                }
+            lse = (m + __builtin_amdgcn_logf(l)) * kLn2;
+        }
+        if (hh == 0) p.lse[part_row0 + qrow] = lse;
+        return;
+    }
     const float inv_l = 1.0f / l;
     uint16_t *O = static_cast<uint16_t *>(p.o) + ((size_t)bh * p.Lq + qrow) * D;
 #pragma unroll
@@ -425,19 +483,30 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         p.lse[(size_t)bh * p.Lq + qrow] = (m + __builtin_amdgcn_logf(l)) * kLn2;
 }
 
+template <bool SPLIT>
+hipError_t launch(const FwdParams &p, int d, bool causal, hipStream_t stream)
+{
+    const dim3 grid(p.n_wg), block(kThreads);
+    if (d == 64) {
+        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, true, SPLIT>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, false, SPLIT>), grid, block, 0, stream, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, true, SPLIT>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, false, SPLIT>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
-    const dim3 grid(p.n_wg), block(kThreads);
-    if (d == 64) {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, false>), grid, block, 0, stream, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, false>), grid, block, 0, stream, p);
-    }
-    return hipGetLastError();
+    return launch<false>(p, d, causal, stream);
+}
+
+hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream)
+{
+    return launch<true>(p, d, causal, stream);
 }
 
 }  // namespace fa2

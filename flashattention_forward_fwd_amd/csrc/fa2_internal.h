@@ -17,7 +17,8 @@ struct FwdParams {
     int B, H, Lq, Lk;
     float scale_log2;   // scale * log2(e): scores are handled in base 2 on the device
     int n_qtiles;       // ceil(Lq / rows per work-group)
-    int n_wg;           // n_qtiles * B * H
+    int n_splits;       // K/V ranges per query tile (1: plain forward)
+    int n_wg;           // n_qtiles * B * H * n_splits
 };
 
 constexpr int kWave = 64;          // CDNA wavefront width
@@ -46,7 +47,7 @@ __device__ __forceinline__ void map_workgroup(int w, int n_wg, int n_qtiles, int
 
 // Number of K/V tiles a query tile visits.  Causal: only tiles holding a key
 // j <= the tile's last valid query row; tiles masked for every row are skipped.
-__device__ __forceinline__ int kv_tiles_for(int qt, int Lq, int Lk, bool causal)
+__host__ __device__ __forceinline__ int kv_tiles_for(int qt, int Lq, int Lk, bool causal)
 {
     int n = (Lk + kBc - 1) / kBc;
     if (causal) {
@@ -70,4 +71,9 @@ __device__ __forceinline__ float swap_halves(float x)
 namespace fa2 {
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t stream);
+// Split-KV partials: p.o is the fp32 partial-output array, p.lse the partial
+// logsumexps, both indexed by (split, b*h, row).
+hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream);
+hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
+                        int d, void *o, float *lse, hipStream_t stream);
 }  // namespace fa2

@@ -55,6 +55,14 @@ WORKLOADS = {
 
 HEADLINE = "B2_H32_L4096_d128_bf16_causal"
 
+# The split-KV (FlashDecoding) scenario: one query per head against a long K/V
+# cache -- the Q-length-1, 128K-context case of "Flash Attention 全解析（上）"
+# sections 4.1 and 4.3.  Same recipe, seed 6.
+DECODE_WORKLOADS = {
+    "B1_H32_Lq1_Lk131072_d128_bf16_decode":
+        Workload("B1_H32_Lq1_Lk131072_d128_bf16_decode", 1, 32, 1, 131072, 128, "bf16", False, 6),
+}
+
 
 def random_qkv(B, H, Lq, Lk, d, dtype="bf16", seed=0, q_mult=1.0):
     """Q [B,H,Lq,d], K and V [B,H,Lk,d] as CPU tensors of the requested dtype."""

@@ -2,7 +2,7 @@
  * fa2.h -- C ABI of the FlashAttention-2 forward library for AMD Instinct MI355X
  * (gfx950), libfa2.so.
  *
- * Operation (both entry points): exact scaled dot-product attention, forward only,
+ * Operation (the forward entry points): exact scaled dot-product attention, forward only,
  * with a per-row logsumexp, for every (batch b, head h, query row i):
  *
  *     s_ij  = scale * (q_i . k_j)            for keys j visible to i
@@ -48,6 +48,9 @@
 #ifndef FA2_H
 #define FA2_H
 
+#include <stddef.h>
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -55,12 +58,15 @@ extern "C" {
 typedef enum fa2_status {
     FA2_OK = 0,
     FA2_ERR_NULL = 1,            /* a tensor pointer is NULL */
-    FA2_ERR_DIM = 2,             /* B, H, Lq or Lk <= 0, or an element count overflows int64 */
+    FA2_ERR_DIM = 2,             /* B, H, Lq or Lk <= 0, an element count overflows int64, the
+                                    grid does not fit, or (Lk + 64) * d * element size of one
+                                    head's K exceeds 2^31 - 1 bytes */
     FA2_ERR_UNSUPPORTED_D = 3,   /* head dimension d not in {64, 128} */
     FA2_ERR_ARG = 4,             /* causal not 0 or 1, or scale not finite or <= 0 */
     FA2_ERR_ALIGN = 5,           /* a tensor pointer is not 16-byte aligned */
     FA2_ERR_DEVICE = 6,          /* no usable HIP device, or the device is not gfx950 */
-    FA2_ERR_LAUNCH = 7           /* the kernel launch was refused by the runtime */
+    FA2_ERR_LAUNCH = 7,          /* the kernel launch was refused by the runtime */
+    FA2_ERR_WORKSPACE = 8        /* workspace NULL or smaller than fa2_splitkv_workspace_bytes */
 } fa2_status;
 
 /*
@@ -83,6 +89,80 @@ int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
  */
 int fa2_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream);
+
+/*
+ * Split-KV forward (FlashDecoding): the same result as fa2_fwd, computed in two
+ * stages on `stream` ("Flash Attention 全解析（上）", section 4.3).
+ *
+ *  1. Every Q block's visible K/V blocks are cut into num_splits contiguous,
+ *     near-equal ranges, and each (Q block, range) pair is an independent
+ *     work-group, so short-Lq or few-head problems still fill the GPU (the
+ *     Q-length-1 problem of section 4.1 of that page).  Each work-group runs the
+ *     fa2_fwd recurrence over its range only and writes, per query row, the
+ *     partial result normalised by its own sum, O_s (fp32, [d]), and its
+ *     logsumexp L_s (fp32, natural log).  A row that sees no key of its range
+ *     gets L_s = -inf and its O_s is left unwritten.
+ *  2. A merge kernel (fa2_merge_partials below) combines the partials of every
+ *     row.
+ *
+ * Arguments as fa2_fwd, plus
+ *   num_splits     : number of K/V ranges, 1..FA2_MAX_SPLITS; 0 picks a count
+ *                    for the current device (fa2_splitkv_num_splits).  Ranges of
+ *                    a Q block with fewer K/V blocks than splits may be empty;
+ *                    such work-groups only mark their rows L_s = -inf.
+ *   workspace      : device memory of at least fa2_splitkv_workspace_bytes(...)
+ *                    bytes, 16-byte aligned, owned by the caller; the call
+ *                    overwrites it and needs no prior contents.  Calls that run
+ *                    at the same time need separate workspaces.
+ *   workspace_bytes: its size; too small -> FA2_ERR_WORKSPACE, nothing launched.
+ * A split count of 1 (given, or chosen for num_splits == 0) runs fa2_fwd's
+ * one-pass kernel and leaves the workspace untouched.
+ */
+#define FA2_MAX_SPLITS 128
+
+int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                    int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes fa2_fwd_splitkv needs for these sizes: num_splits * B * H * Lq
+ * rows of (d + 1) fp32 values, laid out as the partial outputs
+ * [num_splits, B, H, Lq, d] followed (at a 256-byte boundary) by the partial
+ * logsumexps [num_splits, B, H, Lq].  num_splits == 0 resolves as in
+ * fa2_fwd_splitkv (so it needs Lk, causal and the current device).  Returns 0
+ * for sizes fa2_fwd_splitkv would reject.
+ */
+size_t fa2_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int causal, int num_splits);
+
+/*
+ * The split count num_splits == 0 stands for: the fewest ranges that give every
+ * compute unit of the current device one (Q block, range) work-group, or two
+ * when causal (Q blocks then differ in length), with at least 8 K/V blocks per
+ * range and at most FA2_MAX_SPLITS ranges; 1 when the Q blocks alone fill the
+ * device.  Returns 1 if the device cannot be queried.
+ */
+int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal);
+
+/*
+ * Merge n_parts partial attention results of the same queries over disjoint
+ * key sets into the result over their union: for every row r,
+ *     M   = max_s L_s[r]
+ *     W   = sum_s exp(L_s[r] - M)
+ *     O[r]   = sum_s exp(L_s[r] - M) O_s[r] / W      (rounded to bf16, nearest even)
+ *     LSE[r] = M + ln W
+ * i.e. LSE = ln sum_s exp(L_s) and O = sum_s exp(L_s - LSE) O_s, the combine of
+ * two normalised halves in "FlashAttention 怎么做? online softmax 怎么更新?",
+ * follow-up question "多卡(ring attention)怎么合并两段结果?", applied to n parts; it is
+ * also the global rescaling of section 4.3 of "Flash Attention 全解析（上）".
+ * Parts with L_s = -inf contribute nothing and their O_s is not read; a row
+ * whose parts are all -inf gets O = 0 and LSE = -inf.
+ *   o_parts   : fp32 [n_parts, rows, d]    lse_parts : fp32 [n_parts, rows]
+ *   o         : bf16 [rows, d]             lse       : fp32 [rows]
+ *   n_parts 1..FA2_MAX_SPLITS, rows >= 1, d in {64, 128}; device pointers,
+ *   16-byte aligned, caller-owned; outputs must not overlap inputs.
+ */
+int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
+                       int d, void *o, float *lse, void *stream);
 
 /* Static English text for a status code (never NULL). */
 const char *fa2_status_string(int status);

@@ -20,10 +20,11 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu(q, k, v, causal, scale):
-    """q, k, v: CPU tensors.  Returns (o, lse) as float64 numpy arrays."""
+def run_gpu(q, k, v, causal, scale, num_splits=None):
+    """q, k, v: CPU tensors.  Returns (o, lse) as float64 numpy arrays.
+    num_splits None: one-pass kernel; an int: the split-KV path."""
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
-    o, lse = fa.forward(dq, dk, dv, causal=causal, scale=scale)
+    o, lse = fa.forward(dq, dk, dv, causal=causal, scale=scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy()
 
@@ -43,10 +44,11 @@ def compare(name, dtype, o_gpu, lse_gpu, o_ref, lse_ref):
     return eo, el
 
 
-def check_case(name, q, k, v, causal, scale, dtype, rows=None):
+def check_case(name, q, k, v, causal, scale, dtype, rows=None, num_splits=None):
     """Full or row-sampled comparison of the HIP path with the oracle."""
-    say("case %s: B,H,Lq,Lk,d=%s causal=%d" % (name, tuple(q.shape[:3]) + (k.shape[2], q.shape[3]), causal))
-    o_gpu, lse_gpu = run_gpu(q, k, v, causal, scale)
+    say("case %s: B,H,Lq,Lk,d=%s causal=%d splits=%s"
+        % (name, tuple(q.shape[:3]) + (k.shape[2], q.shape[3]), causal, num_splits))
+    o_gpu, lse_gpu = run_gpu(q, k, v, causal, scale, num_splits)
     o_ref, lse_ref = ref.attention_f64(widen(q), widen(k), widen(v), scale, causal, rows=rows)
     if rows is not None:
         B, H = q.shape[:2]

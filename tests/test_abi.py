@@ -20,7 +20,9 @@ def header_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == sorted(["fa2_fwd", "fa2_fwd_f32", "fa2_status_string", "fa2_check_args"])
+    assert header_functions() == sorted(["fa2_fwd", "fa2_fwd_f32", "fa2_status_string", "fa2_check_args",
+                                         "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
+                                         "fa2_splitkv_num_splits", "fa2_merge_partials"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -31,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         assert fa.status_string(code)
     assert fa.status_string(99) == "unknown status"
 
@@ -82,3 +84,46 @@ def test_forward_refuses_host_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.forward(q, q, q)
+
+
+def test_splitkv_rejects_before_touching_the_device():
+    """Bad sizes, split counts and workspaces are refused before any HIP call."""
+    L = fa.lib()
+    f = L.fa2_fwd_splitkv
+    big = 1 << 30
+    assert f(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, 1, A, big, None) == 1
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 0, 1, A, big, None) == 3
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, -1, A, big, None) == 4
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, fa.FA2_MAX_SPLITS + 1, A, big, None) == 4
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, 2, None, big, None) == 8
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, 2, A + 4, big, None) == 5
+
+
+def test_splitkv_workspace_bytes():
+    """Partial outputs [S, rows, d] fp32, padded to 256 bytes, then [S, rows] fp32."""
+    for (B, H, Lq, d, S) in [(1, 1, 1, 64, 1), (2, 3, 100, 128, 4), (1, 2, 77, 64, 3)]:
+        rows = B * H * Lq
+        o_bytes = -(-S * rows * d * 4 // 256) * 256
+        assert fa.fa2_splitkv_workspace_bytes(B, H, Lq, 500, d, 0, S) == o_bytes + S * rows * 4
+    assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 96, 0, 2) == 0
+    assert fa.fa2_splitkv_workspace_bytes(0, 1, 8, 8, 64, 0, 2) == 0
+    assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 64, 0, fa.FA2_MAX_SPLITS + 1) == 0
+
+
+def test_head_size_limit():
+    """One head's K must stay below 2 GiB (32-bit tile offsets)."""
+    # (Lk + 64) * d * element size <= 2^31 - 1
+    assert fa.fa2_check_args(A, A, A, A, A, 1, 1, 8, (1 << 23) - 65, 128, 0.1, 0, 2) == 0
+    assert fa.fa2_check_args(A, A, A, A, A, 1, 1, 8, (1 << 23) - 64, 128, 0.1, 0, 2) == 2
+    assert fa.fa2_check_args(A, A, A, A, A, 1, 1, 8, (1 << 23) - 65, 64, 0.1, 0, 4) == 0
+    assert fa.fa2_check_args(A, A, A, A, A, 1, 1, 8, (1 << 23) - 64, 64, 0.1, 0, 4) == 2
+
+
+def test_merge_rejects_before_touching_the_device():
+    f = fa.lib().fa2_merge_partials
+    assert f(None, A, 2, 10, 64, A, A, None) == 1
+    assert f(A, A, 0, 10, 64, A, A, None) == 4
+    assert f(A, A, fa.FA2_MAX_SPLITS + 1, 10, 64, A, A, None) == 4
+    assert f(A, A, 2, 0, 64, A, A, None) == 2
+    assert f(A, A, 2, 10, 96, A, A, None) == 3
+    assert f(A, A + 4, 2, 10, 64, A, A, None) == 5
