@@ -172,7 +172,7 @@ __device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[2], float c2)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
             mx = fmaxf(mx, s[t][i]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = halves_max(mx);
     return mx * c2;
 }
 
@@ -274,6 +274,9 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
     lpart += rs;
     // Tiles on the causal diagonal or the key tail (few): mask, take the max again.
     if (j + 1 >= n_plain) {
+        // Keeps this block a real branch: otherwise the compiler turns the mask
+        // into selects that run on every tile.
+        asm volatile("");
         mask_scores<CAUSAL>(s_next, (t0 + j + 1) * kBc, Lk, qrow, hh);
         mt = row_max_scaled(s_next, c2);
     }
@@ -448,7 +451,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     }
 
     if (!wave_active) return;
-    const float l = lpart + swap_halves(lpart);
+    const float l = halves_sum(lpart);
     if (qrow >= p.Lq) return;
     if (SPLIT) {
         float lse = -INFINITY;

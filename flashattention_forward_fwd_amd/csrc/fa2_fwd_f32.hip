@@ -126,7 +126,7 @@ void fa2_fwd_f32_kernel(FwdParams p)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 mx = fmaxf(mx, s[t][i]);
-        mx = fmaxf(mx, swap_halves(mx));
+        mx = halves_max(mx);
         const float m_new = fmaxf(m, mx * c2);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
 
@@ -157,7 +157,7 @@ void fa2_fwd_f32_kernel(FwdParams p)
     }
 
     if (!wave_active) return;
-    const float l = lpart + swap_halves(lpart);
+    const float l = halves_sum(lpart);
     if (qrow >= p.Lq) return;
     float *O = static_cast<float *>(p.o) + ((size_t)bh * p.Lq + qrow) * D;
 #pragma unroll

@@ -59,10 +59,28 @@ __host__ __device__ __forceinline__ int kv_tiles_for(int qt, int Lq, int Lk, boo
     return n;
 }
 
-// Exchange with the lane 32 positions away (the other half of the wavefront).
-__device__ __forceinline__ float swap_halves(float x)
+// The two values of a lane pair (l, l + 32), one per wavefront half.  One
+// v_permlane32_swap (a VALU op on gfx950) swaps the upper half of its first
+// operand with the lower half of its second; given x twice, every lane ends up
+// with {own x, partner's x} in some order.
+struct HalfPair {
+    float a, b;
+};
+__device__ __forceinline__ HalfPair half_pair(float x)
 {
-    return __shfl_xor(x, 32, kWave);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+// max / sum of x over the lane pair (l, l + 32); the same value on both lanes.
+__device__ __forceinline__ float halves_max(float x)
+{
+    const HalfPair p = half_pair(x);
+    return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const HalfPair p = half_pair(x);
+    return p.a + p.b;
 }
 
 }  // namespace fa2
