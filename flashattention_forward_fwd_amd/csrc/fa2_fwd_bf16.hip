@@ -274,9 +274,6 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
     lpart += rs;
     // Tiles on the causal diagonal or the key tail (few): mask, take the max again.
     if (j + 1 >= n_plain) {
-        // Keeps this block a real branch: otherwise the compiler turns the mask
-        // into selects that run on every tile.
-        asm volatile("");
         mask_scores<CAUSAL>(s_next, (t0 + j + 1) * kBc, Lk, qrow, hh);
         mt = row_max_scaled(s_next, c2);
     }
