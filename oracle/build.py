@@ -7,17 +7,17 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "attn_ref.c")
+SRCS = [os.path.join(HERE, "attn_ref.c"), os.path.join(HERE, "attn_bwd_ref.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(force: bool = True) -> str:
-    """Compile attn_ref.c into liboracle.so next to it and return the path."""
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+    """Compile the reference sources into liboracle.so next to them and return the path."""
+    if not force and os.path.exists(LIB) and all(os.path.getmtime(LIB) >= os.path.getmtime(s) for s in SRCS):
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"]
+           "-Wall", "-Wextra", "-o", tmp] + SRCS + ["-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

@@ -15,6 +15,8 @@ Three references, each a plain reading of the pages:
   (Q blocks outside, K/V blocks inside, running m and l, unnormalised output, one
   division at the end, logsumexp), used to show on the CPU that the tiled method
   reaches the definition's result.
+* ``attention_bwd_f64`` -- the gradients dQ, dK, dV of the definition (the
+  backward pass), by the chain rule, computed by ``attn_bwd_ref.c``.
 * ``merge_partials`` -- the combine of attention results over disjoint key sets
   from their outputs and logsumexps (ring attention's two-segment merge, and
   FlashDecoding's reduce step).
@@ -41,6 +43,14 @@ def _lib():
             ctypes.c_double, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.oracle_attention_bwd_f64.restype = ctypes.c_int
+        lib.oracle_attention_bwd_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         _LIB = lib
     return _LIB
@@ -95,6 +105,57 @@ def attention_f64(q, k, v, scale, causal, rows=None, nthreads=None):
     if rc != 0:
         raise ValueError("oracle_attention_f64 rejected its arguments (code %d)" % rc)
     return o, lse
+
+
+def _index_rows(idx, BH):
+    """None, or an int64 [B*H, n] array of indices ([n] is shared by every head)."""
+    if idx is None:
+        return None
+    a = np.asarray(idx, dtype=np.int64)
+    if a.ndim == 1:
+        a = np.broadcast_to(a, (BH, a.shape[0]))
+    return np.ascontiguousarray(a.reshape(BH, -1), dtype=np.int64)
+
+
+def attention_bwd_f64(q, k, v, dout, scale, causal, rows=None, keys=None, nthreads=None):
+    """Gradients of exact attention in float64: (dq, dk, dv) for the upstream gradient dout.
+
+    The chain rule through the definition computed by ``attention_f64``:
+    dV = P^T dO, dP = dO V^T, D_i = sum_j P_ij dP_ij, dS = P * (dP - D),
+    dQ = scale dS K, dK = scale dS^T Q.  The pages ask the backward to rebuild
+    S and P from the inputs and the per-row logsumexp instead of storing them
+    ("FlashAttention 怎么做? online softmax 怎么更新?", section "Recomputation");
+    they print no gradient formulas, so these are the derivative written out.
+
+    q, dout: [B, H, Lq, d]; k, v: [B, H, Lk, d].  rows / keys: None for all, else
+    index arrays [B*H, n] (or [n] shared by every head) selecting the query rows
+    of dq and the keys of dk, dv.  Returns dq [B, H, nr, d], dk, dv [B, H, nk, d].
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    dout = np.ascontiguousarray(dout, dtype=np.float64)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    assert k.shape == (B, H, Lk, d) and v.shape == (B, H, Lk, d) and dout.shape == q.shape
+    rows_arr = _index_rows(rows, B * H)
+    keys_arr = _index_rows(keys, B * H)
+    nr = Lq if rows_arr is None else rows_arr.shape[1]
+    nk = Lk if keys_arr is None else keys_arr.shape[1]
+    dq = np.empty((B, H, nr, d))
+    dk = np.empty((B, H, nk, d))
+    dv = np.empty((B, H, nk, d))
+    if nthreads is None:
+        nthreads = default_threads()
+    rc = _lib().oracle_attention_bwd_f64(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+        B, H, Lq, Lk, d, float(scale), int(bool(causal)),
+        rows_arr.ctypes.data if rows_arr is not None else None, nr,
+        keys_arr.ctypes.data if keys_arr is not None else None, nk,
+        dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attention_bwd_f64 rejected its arguments (code %d)" % rc)
+    return dq, dk, dv
 
 
 def softmax_3pass(x):
