@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of the FlashAttention-2 forward pass on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits S]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--splits S] [--backward]
 
 A step is one fa2_fwd call over the whole batch of the workload (inputs already
 resident in device memory); with --splits, one fa2_fwd_splitkv call (partial
-kernel + merge kernel, workspace allocated before the timed region).  Prints ONE JSON line with the throughput in
+kernel + merge kernel, workspace allocated before the timed region); with
+--backward, one fa2_bwd call (prep, dK/dV and dQ kernels) on o and lse from a
+forward call made before the timed region, counted as 2.5x the forward's work
+(10*B*H*Lq*Lk*d, halved for causal: the five products S, dP, dV, dK, dQ).  Prints ONE JSON line with the throughput in
 attention-forward TFLOP/s (4*B*H*Lq*Lk*d, halved for causal), the roofline
 position of the kernel (HIP events on the launch stream), the HBM traffic taken
 from rocprofv3 counters (profiles/), and the CPU oracle timed on a bounded
@@ -24,6 +27,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS (4·B·H·Lq·Lk·d) bf16 at N=2K–16K; % of MFMA peak"
+METRIC_BWD = "attention bwd TFLOPS (10·B·H·Lq·Lk·d, halved for causal) bf16; % of MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X fp32, published
 PEAK_HBM_GBS = 8000.0
@@ -88,6 +92,25 @@ def cpu_baseline(w, q, k, v, rows_per_head):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, do):
+    """The backward oracle, as it stands, on every row and key of the first (batch, head)."""
+    import torch
+    from oracle import ref
+
+    sl = (slice(0, 1), slice(0, 1))
+    qd, kd, vd, dod = (t[sl].to(torch.float64).numpy() for t in (q, k, v, do))
+    threads = ref.default_threads()
+    t0 = time.perf_counter()
+    ref.attention_bwd_f64(qd, kd, vd, dod, w.scale, w.causal, nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.5 * w.flops / (w.B * w.H)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": "full gradients (dq, dk, dv) of 1 of the %d (batch, head) pairs; %.3g FLOP "
+                  "(2.5x the forward count) in %.2f s, fp64" % (w.B * w.H, flops, dt),
+    }
+
+
 def calibrate_copy(nbytes):
     """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
@@ -113,6 +136,8 @@ def main():
                     help="query rows per (batch, head) for the oracle timing (0: every row)")
     ap.add_argument("--splits", type=int, default=None, metavar="S",
                     help="time the split-KV path with S K/V ranges (0: the library's choice)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass fa2_bwd (bf16 workloads) instead of the forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -142,7 +167,25 @@ def main():
     stream = torch.cuda.current_stream()
     args_common = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal))
     split_info = None
-    if args.splits is None:
+    bwd_info = None
+    if args.backward:
+        if w.dtype != "bf16" or args.splits is not None:
+            print("bench.py: --backward takes a bf16 workload and no --splits", file=sys.stderr)
+            sys.exit(2)
+        from flashattention_forward_fwd_amd.inputs import random_dout
+        do = random_dout(w.B, w.H, w.Lq, w.d, "bf16", seed=w.seed)
+        ddo = do.cuda()
+        fa.fa2_fwd(*(args_common + (stream.cuda_stream,)))
+        gq, gk, gv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+        ws_bytes = fa.fa2_bwd_workspace_bytes(w.B, w.H, w.Lq)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        fn = fa.fa2_bwd
+        call = (dq, dk, dv, o, lse, ddo, gq, gk, gv, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal),
+                workspace, ws_bytes, stream.cuda_stream)
+        bwd_info = {"timed_call": "fa2_bwd = prep + dK/dV + dQ kernels", "workspace_bytes": ws_bytes,
+                    "flops_count": "2.5x forward (S, dP, dV, dK, dQ); the dQ pass recomputes S and dP, "
+                                   "so the device executes 3.5x"}
+    elif args.splits is None:
         fn = fa.fa2_fwd if w.dtype == "bf16" else fa.fa2_fwd_f32
         call = args_common + (stream.cuda_stream,)
     else:
@@ -178,11 +221,15 @@ def main():
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     avg_launch_ms = sum(launch_ms) / K
 
-    flops = w.flops
+    flops = w.flops * (2.5 if bwd_info else 1.0)
     value = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    traffic = stored_traffic(w.name) if split_info is None else None
+    traffic = stored_traffic(w.name) if split_info is None and bwd_info is None else None
     algo_bytes = (2 if w.dtype == "bf16" else 4) * w.B * w.H * (2 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq
+    if bwd_info:
+        # reads q, k, v, o, dout, lse; writes dq, dk, dv
+        algo_bytes = 2 * w.B * w.H * (3 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq \
+            + 2 * w.B * w.H * (w.Lq + 2 * w.Lk) * w.d
     # Bound by whichever roof is lower at this arithmetic intensity.
     if flops / algo_bytes >= (peak * 1e12) / (PEAK_HBM_GBS * 1e9):
         roof = {"bound": "mfma", "achieved": round(flops / (avg_launch_ms * 1e-3) / 1e12, 2), "peak": peak,
@@ -195,7 +242,7 @@ def main():
                  "min_launch_ms": round(min(launch_ms), 5)})
 
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "metric": METRIC_BWD if bwd_info else METRIC, "value": round(value, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
@@ -207,7 +254,11 @@ def main():
     }
     if split_info is not None:
         out["config"]["split_kv"] = split_info
-    if not args.no_cpu_baseline:
+    if bwd_info is not None:
+        out["config"]["backward"] = bwd_info
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do)
+    elif not args.no_cpu_baseline:
         n = args.cpu_rows_per_head if args.cpu_rows_per_head > 0 else w.Lq
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(n, w.Lq))
     print(json.dumps(out), flush=True)

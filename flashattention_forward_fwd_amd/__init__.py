@@ -1,4 +1,4 @@
-"""FlashAttention-2 forward for AMD Instinct MI355X (gfx950).
+"""FlashAttention-2 forward (and backward) for AMD Instinct MI355X (gfx950).
 
 The computation lives in the HIP library libfa2.so (C ABI in include/fa2.h);
 this package only marshals arguments to it.  PyTorch provides device memory
@@ -6,16 +6,18 @@ and the stream.
 
     from flashattention_forward_fwd_amd import forward
     o, lse = forward(q, k, v, causal=True)      # q [B,H,Lq,d], k/v [B,H,Lk,d] on cuda
+    dq, dk, dv = backward(q, k, v, o, lse, do, causal=True)
 """
 import math
 
-from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_check_args, fa2_fwd, fa2_fwd_f32,  # noqa: F401
-                   fa2_fwd_splitkv, fa2_merge_partials, fa2_splitkv_num_splits,
-                   fa2_splitkv_workspace_bytes, lib, status_string)
+from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_workspace_bytes,  # noqa: F401
+                   fa2_check_args, fa2_fwd, fa2_fwd_f32, fa2_fwd_splitkv, fa2_merge_partials,
+                   fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib, status_string)
 
-__all__ = ["forward", "merge_partials", "fa2_fwd", "fa2_fwd_f32", "fa2_fwd_splitkv",
+__all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f32", "fa2_fwd_splitkv",
            "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
-           "fa2_check_args", "FA2Error", "status_string", "FA2_MAX_SPLITS"]
+           "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
+           "FA2_MAX_SPLITS"]
 
 
 def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, workspace=None):
@@ -92,3 +94,44 @@ def merge_partials(o_parts, lse_parts, out=None, lse=None):
     stream = torch.cuda.current_stream(o_parts.device).cuda_stream
     fa2_merge_partials(o_parts, lse_parts, S, rows, d, out, lse, stream)
     return out, lse
+
+
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of attention for the upstream gradient dout (libfa2 ``fa2_bwd``).
+
+    q, k, v, o, dout: bfloat16 CUDA tensors (q, o, dout [B, H, Lq, d]; k, v
+    [B, H, Lk, d]), o and lse (fp32 [B, H, Lq]) as returned by ``forward`` for
+    the same q, k, v, causal and scale.  Returns bf16 (dq, dk, dv).  The
+    workspace is allocated here unless a large enough uint8 device tensor is
+    given.  Enqueued on the current stream.
+    """
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if not all(t.is_cuda for t in ts) or not lse.is_cuda:
+        raise ValueError("all tensors must be device tensors (no CPU path)")
+    if any(t.dtype != torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, o, dout must be bfloat16 and lse float32")
+    if any(t.dim() != 4 for t in ts):
+        raise ValueError("q, k, v, o, dout must be [B, H, L, d]")
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
+        raise ValueError("k and v must be [B, H, Lk, d] matching q")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Lq):
+        raise ValueError("o and dout must have q's shape and lse [B, H, Lq]")
+    q, k, v, o, dout, lse = (t.contiguous() for t in (q, k, v, o, dout, lse))
+    if scale is None:
+        scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa2_bwd_workspace_bytes(B, H, Lq)
+    if need == 0:
+        raise ValueError("sizes rejected by fa2_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), workspace,
+            workspace.numel() * workspace.element_size(), stream)
+    return dq, dk, dv

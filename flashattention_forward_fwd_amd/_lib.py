@@ -1,6 +1,6 @@
 """ctypes binding of libfa2.so -- argument marshalling only.
 
-Every step of the forward pass runs in the HIP library.  There is no fallback:
+Every step of the forward and backward passes runs in the HIP library.  There is no fallback:
 if libfa2.so is missing or fails to load, every entry point raises.
 """
 import ctypes
@@ -32,6 +32,8 @@ SIGNATURES = {
     "fa2_splitkv_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "fa2_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fa2_merge_partials": (_I, [_P, _P, _I, _L, _I, _P, _P, _P]),
+    "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
+    "fa2_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
 }
 
 _lib = None
@@ -125,3 +127,18 @@ def fa2_merge_partials(o_parts, lse_parts, n_parts, rows, d, o, lse, stream):
                                   _ptr(o), _ptr(lse), _ptr(stream))
     if st != FA2_OK:
         raise FA2Error(st, "fa2_merge_partials")
+
+
+def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+            workspace_bytes, stream):
+    """libfa2 ``fa2_bwd`` (bf16 gradients dq, dk, dv).  Raises FA2Error."""
+    st = lib().fa2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                       _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                       _ptr(workspace), int(workspace_bytes), _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_bwd")
+
+
+def fa2_bwd_workspace_bytes(B, H, Lq):
+    """libfa2 ``fa2_bwd_workspace_bytes``: bytes of backward workspace (0: sizes rejected)."""
+    return lib().fa2_bwd_workspace_bytes(int(B), int(H), int(Lq))

@@ -145,6 +145,55 @@ size_t workspace_bytes(int64_t S, int B, int H, int Lq, int d)
     return partial_o_bytes(S, rows, d) + (size_t)S * rows * sizeof(float);
 }
 
+// Backward workspace: lse * log2(e) for every query row, then (at a 256-byte
+// boundary) D = rowsum(dO * O) for every query row, both fp32.  0 on overflow.
+size_t bwd_lse2_bytes(int64_t rows)
+{
+    return ((size_t)rows * sizeof(float) + 255) & ~(size_t)255;
+}
+size_t bwd_workspace_bytes(int B, int H, int Lq)
+{
+    if (B <= 0 || H <= 0 || Lq <= 0) return 0;
+    if (!product_fits(B, H, Lq, 2 * sizeof(float))) return 0;
+    const int64_t rows = (int64_t)B * H * Lq;
+    return bwd_lse2_bytes(rows) + (size_t)rows * sizeof(float);
+}
+
+int prepare_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                const void *dq, const void *dk, const void *dv, int B, int H, int Lq, int Lk, int d,
+                float scale, int causal, const void *workspace, size_t workspace_bytes_given,
+                fa2::BwdParams *out)
+{
+    if (!dout || !dq || !dk || !dv) return FA2_ERR_NULL;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, nullptr);
+    if (st != FA2_OK) return st;
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return FA2_ERR_ALIGN;
+    // Query tiles of one head are addressed with 32-bit buffer offsets too.
+    if (((int64_t)Lq + fa2::kBr) * d * 2 > INT32_MAX) return FA2_ERR_DIM;
+    const int64_t key_blocks = (Lk + 127) / 128;
+    if ((int64_t)B * H > INT32_MAX / key_blocks) return FA2_ERR_DIM;          // dK/dV grid
+    const int64_t rows = (int64_t)B * H * Lq;
+    if (rows * (d / 8) / 256 + 1 > INT32_MAX) return FA2_ERR_DIM;             // prep grid
+    const size_t need = bwd_workspace_bytes(B, H, Lq);
+    if (need == 0) return FA2_ERR_DIM;
+    if (!workspace) return FA2_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA2_ERR_ALIGN;
+    if (workspace_bytes_given < need) return FA2_ERR_WORKSPACE;
+    if (out) {
+        out->q = q; out->k = k; out->v = v; out->dout = dout;
+        out->dq = const_cast<void *>(dq); out->dk = const_cast<void *>(dk); out->dv = const_cast<void *>(dv);
+        float *ws = static_cast<float *>(const_cast<void *>(workspace));
+        out->lse2 = ws;
+        out->delta = reinterpret_cast<const float *>(reinterpret_cast<const char *>(ws) + bwd_lse2_bytes(rows));
+        out->B = B; out->H = H; out->Lq = Lq; out->Lk = Lk;
+        out->scale = scale;
+        out->scale_log2 = (float)((double)scale * 1.4426950408889634074);
+        out->n_blocks = 0;
+        out->n_wg = 0;
+    }
+    return FA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,6 +301,25 @@ int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts
     return FA2_OK;
 }
 
+size_t fa2_bwd_workspace_bytes(int B, int H, int Lq)
+{
+    return bwd_workspace_bytes(B, H, Lq);
+}
+
+int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+            void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
+            void *workspace, size_t workspace_bytes_given, void *stream)
+{
+    fa2::BwdParams p;
+    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+                         workspace_bytes_given, &p);
+    if (st != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (fa2::launch_bwd_bf16(p, d, causal != 0, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
 const char *fa2_status_string(int status)
 {
     switch (status) {
@@ -263,7 +331,7 @@ const char *fa2_status_string(int status)
     case FA2_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
-    case FA2_ERR_WORKSPACE: return "split-KV workspace missing or too small";
+    case FA2_ERR_WORKSPACE: return "workspace missing or too small";
     default: return "unknown status";
     }
 }

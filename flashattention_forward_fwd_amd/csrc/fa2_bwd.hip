@@ -1,0 +1,483 @@
+// fa2_bwd.hip -- FlashAttention-2 backward pass, bf16 in/out, for gfx950.
+//
+// The backward needs the probabilities P of the forward but the forward keeps
+// only O and one logsumexp per row, so every score block is rebuilt from Q, K
+// and the saved logsumexp ("FlashAttention 怎么做? online softmax 怎么更新?",
+// section "Recomputation").  With P = exp(scale * Q K^T - LSE) (masked keys 0)
+// and dO the gradient of O, the gradients are the derivative of the forward
+// definition:
+//   D_i = sum_t dO_it O_it        (= sum_j P_ij dP_ij)
+//   dV  = P^T dO                  dP = dO V^T
+//   dS  = P * (dP - D)            dQ = scale dS K        dK = scale dS^T Q
+//
+// Three kernels, enqueued in order on one stream, no atomics (run-to-run
+// bitwise identical results):
+//  1. prep: per row, D_i and lse_i * log2(e) into the caller's workspace.
+//  2. dK/dV: one work-group per block of 128 keys of one (batch, head); each
+//     wavefront keeps K and V of its 32 keys in registers and accumulates dK^T
+//     and dV^T of those keys while 32-row tiles of Q and dO (and their D and
+//     lse) stream through LDS.  Under the causal mask only the query tiles at
+//     or below the block's first key are visited.
+//  3. dQ: one work-group per tile of 128 query rows, laid out like the forward
+//     kernel: each wavefront keeps Q and dO of its 32 rows in registers and
+//     accumulates dQ^T while 64-key tiles of K and V stream through LDS.
+// dQ is computed by its own pass (S and dP rebuilt a second time) instead of
+// being accumulated across key blocks with atomics, which would make the sum
+// order, and so the rounding, depend on scheduling.
+//
+// Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A
+// 32x32 score accumulator puts one key (dK/dV kernel) or one query (dQ kernel)
+// on each lane with 16 entries of the other index, in groups of four; that is
+// the operand layout of the following product once the contraction index is
+// permuted the same way on both operands, so P and dS feed the next MFMA
+// straight from registers (rounded to bf16, nearest even).  Operands whose
+// contraction index runs down the rows of a row-major LDS tile (dO^T, Q^T, K^T)
+// come from the gfx950 transposing LDS read ds_read_b64_tr_b16.
+#include "fa2_internal.h"
+
+namespace fa2 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kRawBufferFlags = 0x00020000;   // raw buffer access, gfx9 resource word 3
+constexpr float kLog2e = 1.44269504088896340736f;
+
+constexpr int kKeysPerWave = 32;                  // dK/dV: keys owned by one wavefront
+constexpr int kKeyBlock = kWaves * kKeysPerWave;  // dK/dV: keys per work-group
+constexpr int kRowTile = 32;                      // dK/dV: query rows per LDS tile
+
+// A row-major bf16 tile [rows][D] in LDS, its 16-byte chunks XOR-swizzled by
+// row.  The swizzle serves both read patterns the backward uses:
+//  * ds_read_b128 of one logical chunk from 16 consecutive rows (the A operand
+//    of a product contracting over d): the rows land in 16 different chunks;
+//  * ds_read_b64_tr_b16 of 4 consecutive rows x 4 consecutive logical chunks
+//    (the transposed A operand): the 4 rows land in 4 different aligned groups
+//    of 4 chunks, so the 16 (row, chunk) pairs are 16 different chunks.
+// For d = 64 two rows share one 256-byte line; the row parity separates them.
+template <int D> struct BTile {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kChunks = kRowBytes / 16;
+    static constexpr int kRowsPerXfer = 1024 / kRowBytes;   // rows per 1 KiB DMA transfer
+    static __device__ __forceinline__ int swz(int r)
+    {
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+    }
+    // Byte address in the tile of logical byte x of row r.
+    static __device__ __forceinline__ int addr(int r, int x)
+    {
+        return r * kRowBytes + 16 * ((x >> 4) ^ swz(r)) + (x & 15);
+    }
+};
+
+// Issue this wavefront's share of the asynchronous HBM -> LDS copy of rows
+// [row0, row0 + ROWS) of a [*, D] bf16 tensor into an LDS tile (swizzled as
+// BTile).  Rows past the end of the buffer range arrive as zeros.  Transfer b
+// moves 1 KiB: lane l lands at byte 16 l, i.e. row b * rows_per_xfer + l / chunks
+// and physical chunk l % chunks, and reads that row's logical chunk.
+template <int D, int ROWS>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t src, int row0, uint16_t *dst, int wave, int lane)
+{
+    using T = BTile<D>;
+    constexpr int kXfers = ROWS * T::kRowBytes / 1024;
+    static_assert(kXfers % kWaves == 0, "tile must split evenly over the wavefronts");
+#pragma unroll
+    for (int x = 0; x < kXfers / kWaves; ++x) {
+        const int b = wave * (kXfers / kWaves) + x;
+        const int r = b * T::kRowsPerXfer + lane / T::kChunks;
+        const int phys = lane % T::kChunks;
+        // The whole offset goes in the VGPR operand, which the range check covers.
+        const int voff = (row0 + r) * T::kRowBytes + 16 * (phys ^ T::swz(r));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void *)(dst + b * 512), 16, voff, 0, 0, 0);
+    }
+}
+
+// A operand contracting over d: row `row` of a tile, logical d chunk 16c + 8hh.
+template <int D>
+__device__ __forceinline__ bf16x8 read_rows_op(const LDS_AS char *tile, int row, int c, int hh)
+{
+    return *reinterpret_cast<const LDS_AS bf16x8 *>(tile + BTile<D>::addr(row, 2 * (16 * c + 8 * hh)));
+}
+
+// Transposed A operand for a product contracting over the tile's rows: lane l
+// receives column 32 dt + l % 32 at rows 16c + 4hh + 0..3 (slots 0-3) and
+// 16c + 8 + 4hh + 0..3 (slots 4-7), hh = l / 32.  Lane 16g + 4e + r supplies the
+// address of row 4(g/2) + e (+16c, +8 for the second read), columns
+// 32 dt + 16(g%2) + 4r .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 read_cols_op(const LDS_AS char *tile, int dt, int c, int lane)
+{
+    const int g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
+    const int row = 16 * c + 4 * (g >> 1) + e;
+    const int x = 2 * (32 * dt + 16 * (g & 1) + 4 * r);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(tile + BTile<D>::addr(row, x)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(tile + BTile<D>::addr(row + 8, x)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 16 bytes of a bf16 row from global memory (zero when `valid` is false).
+__device__ __forceinline__ bf16x8 load_row_chunk(const uint16_t *p, bool valid)
+{
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (valid) raw = *reinterpret_cast<const u32x4 *>(p);
+    return __builtin_bit_cast(bf16x8, raw);
+}
+
+// Store one lane's share of a transposed accumulator (rows = d, columns =
+// token) as bf16: the lane holds column l % 32 (token `row`), d positions
+// 32 dt + 8a + 4hh + 0..3 in accumulator entries 4a .. 4a+3.
+template <int D>
+__device__ __forceinline__ void store_tokens(uint16_t *dst_row, const f32x16 (&acc)[D / 32], float mul, int hh)
+{
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x4 v4 = {acc[dt][4 * a + 0] * mul, acc[dt][4 * a + 1] * mul, acc[dt][4 * a + 2] * mul,
+                              acc[dt][4 * a + 3] * mul};
+            *reinterpret_cast<bf16x4 *>(dst_row + 32 * dt + 8 * a + 4 * hh) = __builtin_convertvector(v4, bf16x4);
+        }
+}
+
+// ---------------------------------------------------------------- 1. prep
+// D_i = sum_t dO_it O_it (fp32) and lse2_i = lse_i * log2(e); D/8 threads per row.
+template <int D>
+__global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, const uint16_t *dout, const float *lse,
+                                                           float *lse2, float *delta, int64_t rows)
+{
+    constexpr int kTpr = D / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid / kTpr;
+    const int part = (int)(gid % kTpr);
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(o + row * D + 8 * part);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(dout + row * D + 8 * part);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc = __builtin_fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
+            acc = __builtin_fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int off = kTpr / 2; off > 0; off >>= 1)
+        acc += __shfl_xor(acc, off, kTpr);
+    if (row < rows && part == 0) {
+        delta[row] = acc;
+        lse2[row] = lse[row] * kLog2e;
+    }
+}
+
+// ---------------------------------------------------------------- 2. dK, dV
+// Work-group id -> (batch*head, key block).  Under the causal mask the first
+// key block sees the most query tiles, so blocks run from the first to the last
+// across all heads (longest first); heads are the fast index.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fa2_bwd_dkdv_kernel(BwdParams p)
+{
+    using T = BTile<D>;
+    constexpr int kDc = D / 16;
+    constexpr int kDt = D / 32;
+    constexpr int kTileElems = kRowTile * D;
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sO0[kTileElems];   // dO tiles
+    __shared__ __attribute__((aligned(1024))) uint16_t sO1[kTileElems];
+    // per buffer: lse2 of 64 rows (first 32 used), then D of 64 rows
+    __shared__ __attribute__((aligned(256))) float sStat0[128];
+    __shared__ __attribute__((aligned(256))) float sStat1[128];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const int n_bh = p.B * p.H;
+    const int bh = blockIdx.x % n_bh;
+    const int kb = blockIdx.x / n_bh;
+    const int kw0 = kb * kKeyBlock + wave * kKeysPerWave;   // first key of this wavefront
+    const int key = kw0 + l32;                              // this lane's key
+    const int n_qt = (p.Lq + kRowTile - 1) / kRowTile;
+    // Query tiles [t0, n_qt) of the work-group; this wavefront computes from wt0.
+    const int t0 = CAUSAL ? min(kb * (kKeyBlock / kRowTile), n_qt) : 0;
+    const int wt0 = CAUSAL ? min(kw0 / kRowTile, n_qt) : 0;
+
+    const size_t row_off = (size_t)bh * p.Lq;
+    const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.q) + row_off * D), 0, p.Lq * T::kRowBytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.dout) + row_off * D), 0, p.Lq * T::kRowBytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.lse2 + row_off), 0, p.Lq * 4, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.delta + row_off), 0, p.Lq * 4, kRawBufferFlags);
+
+    // Tile t: Q and dO rows into the buffers of parity (t - t0), lse2 (wave 0)
+    // and D (wave 1) of rows 32t .. 32t + 63 into the stats buffer.
+    auto load = [&](int t, uint16_t *q_dst, uint16_t *o_dst, float *st_dst) {
+        load_tile<D, kRowTile>(rQ, t * kRowTile, q_dst, wave, lane);
+        load_tile<D, kRowTile>(rO, t * kRowTile, o_dst, wave, lane);
+        if (wave < 2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rL : rD, (LDS_AS void *)(st_dst + 64 * wave), 4,
+                                                     4 * (t * kRowTile + lane), 0, 0, 0);
+    };
+    if (t0 < n_qt) load(t0, sQ0, sO0, sStat0);
+
+    // K and V of this lane's key as B operands (d chunk 16c + 8hh); zero past Lk.
+    const uint16_t *Kr = static_cast<const uint16_t *>(p.k) + ((size_t)bh * p.Lk + key) * D;
+    const uint16_t *Vr = static_cast<const uint16_t *>(p.v) + ((size_t)bh * p.Lk + key) * D;
+    bf16x8 kf[kDc], vf[kDc];
+#pragma unroll
+    for (int c = 0; c < kDc; ++c) {
+        kf[c] = load_row_chunk(Kr + 16 * c + 8 * hh, key < p.Lk);
+        vf[c] = load_row_chunk(Vr + 16 * c + 8 * hh, key < p.Lk);
+    }
+
+    f32x16 acc_dk[kDt], acc_dv[kDt];
+#pragma unroll
+    for (int t = 0; t < kDt; ++t) {
+        acc_dk[t] = f32x16{};
+        acc_dv[t] = f32x16{};
+    }
+    const float c2 = p.scale_log2;
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int t = t0; t < n_qt; ++t) {
+        const bool odd = (t - t0) & 1;
+        if (t + 1 < n_qt) {
+            if (odd) load(t + 1, sQ0, sO0, sStat0);
+            else     load(t + 1, sQ1, sO1, sStat1);
+        }
+        const LDS_AS char *qb = (const LDS_AS char *)(odd ? sQ1 : sQ0);
+        const LDS_AS char *ob = (const LDS_AS char *)(odd ? sO1 : sO0);
+        const LDS_AS float *st = (const LDS_AS float *)(odd ? sStat1 : sStat0);
+        if (t >= wt0) {
+            // S = Q K^T and dP = dO V^T for 32 rows x this wavefront's 32 keys.
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int c = 0; c < kDc; ++c)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(qb, l32, c, hh), kf[c], s, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < kDc; ++c)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(ob, l32, c, hh), vf[c], dp, 0, 0, 0);
+            // Entry i of the accumulators is row 8(i/4) + 4hh + i%4 of the tile.
+            f32x4 l4[4], d4[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                l4[g] = *reinterpret_cast<const LDS_AS f32x4 *>(st + 8 * g + 4 * hh);
+                d4[g] = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 8 * g + 4 * hh);
+            }
+            const bool diag = CAUSAL && t == wt0;   // rows of this tile before a key mask it
+            bf16x8 pf[2], dsf[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                f32x8 p8, ds8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 8 * c + e;
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l4[i / 4][i % 4]));
+                    if (diag) {
+                        const int row = t * kRowTile + 8 * (i / 4) + 4 * hh + (i % 4);
+                        pv = key > row ? 0.f : pv;
+                    }
+                    p8[e] = pv;
+                    ds8[e] = pv * (dp[i] - d4[i / 4][i % 4]);
+                }
+                pf[c] = __builtin_convertvector(p8, bf16x8);
+                dsf[c] = __builtin_convertvector(ds8, bf16x8);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's rows).
+#pragma unroll
+            for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    acc_dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(ob, dt, c, lane), pf[c],
+                                                                         acc_dv[dt], 0, 0, 0);
+                    acc_dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(qb, dt, c, lane), dsf[c],
+                                                                         acc_dk[dt], 0, 0, 0);
+                }
+        }
+        __builtin_amdgcn_s_waitcnt(0);        // this wave's loads of tile t+1 have landed
+        __syncthreads();                      // ... everyone's, and tile t's buffers are free
+    }
+
+    if (key >= p.Lk) return;
+    const size_t kv_row = (size_t)bh * p.Lk + key;
+    store_tokens<D>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc_dk, p.scale, hh);
+    store_tokens<D>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc_dv, 1.0f, hh);
+}
+
+// ---------------------------------------------------------------- 3. dQ
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void fa2_bwd_dq_kernel(BwdParams p)
+{
+    using T = BTile<D>;
+    constexpr int kDc = D / 16;
+    constexpr int kDt = D / 32;
+    constexpr int kTileElems = kBc * D;
+    __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV1[kTileElems];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    int bh, qt;
+    map_workgroup(blockIdx.x, p.n_wg, p.n_blocks, bh, qt);
+    const int n_kv = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
+
+    const size_t kv_off = (size_t)bh * p.Lk * D;
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.k) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.v) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+
+    const int q0 = qt * kBr + wave * kRowsPerWave;
+    const int qrow = q0 + l32;
+    const bool row_ok = qrow < p.Lq;
+    const bool wave_active = q0 < p.Lq;
+
+    // K/V tiles this wavefront computes: [0, n_plain) unmasked, [n_plain, n_wave)
+    // crossing the diagonal or the end of the keys (as in the forward kernel).
+    int n_wave = 0, n_plain = 0;
+    if (wave_active) {
+        const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
+        const int end = CAUSAL ? min(n_kv, wave_qlast / kBc + 1) : n_kv;
+        int plain = p.Lk / kBc;
+        if (CAUSAL) plain = min(plain, (q0 + 1) / kBc);
+        n_wave = end;
+        n_plain = min(plain, n_wave);
+    }
+
+    load_tile<D, kBc>(rK, 0, sK0, wave, lane);
+    load_tile<D, kBc>(rV, 0, sV0, wave, lane);
+
+    const size_t qoff = ((size_t)bh * p.Lq + qrow);
+    const uint16_t *Qr = static_cast<const uint16_t *>(p.q) + qoff * D;
+    const uint16_t *Or = static_cast<const uint16_t *>(p.dout) + qoff * D;
+    bf16x8 qf[kDc], of[kDc];
+#pragma unroll
+    for (int c = 0; c < kDc; ++c) {
+        qf[c] = load_row_chunk(Qr + 16 * c + 8 * hh, row_ok);
+        of[c] = load_row_chunk(Or + 16 * c + 8 * hh, row_ok);
+    }
+    const float lse2 = row_ok ? p.lse2[qoff] : 0.f;
+    const float dlt = row_ok ? p.delta[qoff] : 0.f;
+
+    f32x16 acc[kDt];
+#pragma unroll
+    for (int t = 0; t < kDt; ++t)
+        acc[t] = f32x16{};
+    const float c2 = p.scale_log2;
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    for (int j = 0; j < n_kv; ++j) {
+        const bool odd = j & 1;
+        if (j + 1 < n_kv) {
+            load_tile<D, kBc>(rK, (j + 1) * kBc, odd ? sK0 : sK1, wave, lane);
+            load_tile<D, kBc>(rV, (j + 1) * kBc, odd ? sV0 : sV1, wave, lane);
+        }
+        const LDS_AS char *kbuf = (const LDS_AS char *)(odd ? sK1 : sK0);
+        const LDS_AS char *vbuf = (const LDS_AS char *)(odd ? sV1 : sV0);
+        if (j < n_wave) {
+            // S^T = K Q^T and dP^T = V dO^T: (keys x this wavefront's queries).
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                s[t] = f32x16{};
+                dp[t] = f32x16{};
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(kbuf, 32 * t + l32, c, hh), qf[c],
+                                                                   s[t], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(vbuf, 32 * t + l32, c, hh), of[c],
+                                                                    dp[t], 0, 0, 0);
+            }
+            // Entry i of tile t is key 64j + 32t + 8(i/4) + 4hh + i%4.
+            const bool need_mask = j >= n_plain;
+            bf16x8 dsf[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int t = c >> 1, i0 = 8 * (c & 1);
+                f32x8 ds8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = i0 + e;
+                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -lse2));
+                    if (need_mask) {
+                        const int kk = j * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
+                        pv = (kk >= p.Lk || (CAUSAL && kk > qrow)) ? 0.f : pv;
+                    }
+                    ds8[e] = pv * (dp[t][i] - dlt);
+                }
+                dsf[c] = __builtin_convertvector(ds8, bf16x8);
+            }
+            // dQ^T += K^T dS^T (contraction over the tile's keys).
+#pragma unroll
+            for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(kbuf, dt, c, lane), dsf[c],
+                                                                      acc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    if (!row_ok) return;
+    store_tokens<D>(static_cast<uint16_t *>(p.dq) + qoff * D, acc, p.scale, hh);
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams &p, bool causal, int64_t rows, const void *o, const float *lse,
+                        hipStream_t stream)
+{
+    const int64_t threads = rows * (D / 8);
+    hipLaunchKernelGGL((fa2_bwd_prep_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(p.dout), lse,
+                       const_cast<float *>(p.lse2), const_cast<float *>(p.delta), rows);
+    BwdParams pk = p;
+    pk.n_blocks = (p.Lk + kKeyBlock - 1) / kKeyBlock;
+    pk.n_wg = pk.n_blocks * p.B * p.H;
+    if (causal) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true>), dim3(pk.n_wg), dim3(kThreads), 0, stream, pk);
+    else        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false>), dim3(pk.n_wg), dim3(kThreads), 0, stream, pk);
+    BwdParams pq = p;
+    pq.n_blocks = (p.Lq + kBr - 1) / kBr;
+    pq.n_wg = pq.n_blocks * p.B * p.H;
+    if (causal) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, bool causal, const void *o, const float *lse,
+                           hipStream_t stream)
+{
+    const int64_t rows = (int64_t)p.B * p.H * p.Lq;
+    return d == 64 ? launch_bwd_d<64>(p, causal, rows, o, lse, stream)
+                   : launch_bwd_d<128>(p, causal, rows, o, lse, stream);
+}
+
+}  // namespace fa2

@@ -21,6 +21,25 @@ struct FwdParams {
     int n_wg;           // n_qtiles * B * H * n_splits
 };
 
+// Everything a backward kernel needs (q, k, v, dout bf16 inputs; dq, dk, dv bf16
+// outputs; lse2 = lse * log2(e) and delta = rowsum(dO * O), fp32 per query row).
+struct BwdParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *dout;
+    void *dq;
+    void *dk;
+    void *dv;
+    const float *lse2;
+    const float *delta;
+    int B, H, Lq, Lk;
+    float scale;        // softmax scale; dQ and dK are multiplied by it
+    float scale_log2;   // scale * log2(e)
+    int n_blocks;       // per head: key blocks (dK/dV kernel) or query tiles (dQ kernel)
+    int n_wg;           // n_blocks * B * H
+};
+
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kWaves = 4;          // wavefronts per work-group
 constexpr int kThreads = kWave * kWaves;
@@ -92,6 +111,9 @@ hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t st
 // Split-KV partials: p.o is the fp32 partial-output array, p.lse the partial
 // logsumexps, both indexed by (split, b*h, row).
 hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream);
+// Backward: D and lse2 into p.delta / p.lse2 from o and lse, then dK/dV, then dQ.
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, bool causal, const void *o, const float *lse,
+                           hipStream_t stream);
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                         int d, void *o, float *lse, hipStream_t stream);
 }  // namespace fa2

@@ -77,6 +77,16 @@ def random_qkv(B, H, Lq, Lk, d, dtype="bf16", seed=0, q_mult=1.0):
     return tq.contiguous(), tk.contiguous(), tv.contiguous()
 
 
+def random_dout(B, H, Lq, d, dtype="bf16", seed=0):
+    """Upstream gradient dO [B,H,Lq,d] for the backward pass: fp32 iid N(0, 1) from its
+    own generator (seed sequence [seed, 4], so Q, K, V of the same seed are unchanged),
+    rounded to the requested dtype like Q, K, V."""
+    rng = np.random.default_rng([seed, 4])
+    a = rng.standard_normal((B, H, Lq, d), dtype=np.float32)
+    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    return torch.from_numpy(a).to(tdt).contiguous()
+
+
 def workload_inputs(w: Workload):
     return random_qkv(w.B, w.H, w.Lq, w.Lk, w.d, w.dtype, w.seed, w.q_mult)
 

@@ -1,6 +1,7 @@
 /*
- * fa2.h -- C ABI of the FlashAttention-2 forward library for AMD Instinct MI355X
- * (gfx950), libfa2.so.
+ * fa2.h -- C ABI of the FlashAttention-2 library for AMD Instinct MI355X (gfx950),
+ * libfa2.so: the forward pass (one-pass and split-KV), the merge of partial
+ * results, and the backward pass.
  *
  * Operation (the forward entry points): exact scaled dot-product attention, forward only,
  * with a per-row logsumexp, for every (batch b, head h, query row i):
@@ -66,7 +67,8 @@ typedef enum fa2_status {
     FA2_ERR_ALIGN = 5,           /* a tensor pointer is not 16-byte aligned */
     FA2_ERR_DEVICE = 6,          /* no usable HIP device, or the device is not gfx950 */
     FA2_ERR_LAUNCH = 7,          /* the kernel launch was refused by the runtime */
-    FA2_ERR_WORKSPACE = 8        /* workspace NULL or smaller than fa2_splitkv_workspace_bytes */
+    FA2_ERR_WORKSPACE = 8        /* workspace NULL or smaller than fa2_splitkv_workspace_bytes /
+                                    fa2_bwd_workspace_bytes */
 } fa2_status;
 
 /*
@@ -163,6 +165,46 @@ int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal);
  */
 int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                        int d, void *o, float *lse, void *stream);
+
+/*
+ * Backward pass (gradients) of fa2_fwd, bf16.  Given the forward's inputs, its
+ * outputs o and lse, and dout = dL/dO, computes dq = dL/dQ, dk = dL/dK and
+ * dv = dL/dV of the same attention (same scale, same causal mask):
+ *
+ *     P    = exp(scale * Q K^T - LSE)             (masked keys: 0)
+ *     D_i  = sum_t dout_it o_it
+ *     dV   = P^T dout          dP = dout V^T       dS = P * (dP - D)
+ *     dQ   = scale * dS K      dK = scale * dS^T Q
+ *
+ * The score and probability blocks are rebuilt from q, k and lse instead of
+ * being stored by the forward ("FlashAttention 怎么做? online softmax 怎么更新?",
+ * section "Recomputation"); the formulas are the derivative of the forward
+ * definition.  Products run on bf16 matrix cores with fp32 accumulation; P and
+ * dS are rounded to bf16 (nearest even) before they enter a product; dq, dk, dv
+ * are rounded to bf16 (nearest even).  dQ is computed by a pass of its own over
+ * the key blocks rather than accumulated with atomics, so results are
+ * run-to-run bitwise identical.
+ *   q, k, v, o, dout : bf16 device pointers; q, o, dout [B, H, Lq, d], k, v [B, H, Lk, d]
+ *   lse              : fp32 [B, H, Lq], as written by fa2_fwd for these q, k, v
+ *   dq, dk, dv       : bf16 outputs, shapes of q, k, v; completely overwritten (keys
+ *                      that no query sees under the causal mask get 0)
+ *   workspace        : device memory of at least fa2_bwd_workspace_bytes(B, H, Lq)
+ *                      bytes, 16-byte aligned, caller-owned; overwritten, needs no
+ *                      prior contents; concurrent calls need separate workspaces
+ * Other arguments, layout and error rules as fa2_fwd; additionally
+ * FA2_ERR_WORKSPACE for a missing or too small workspace.  Outputs must not
+ * overlap inputs or each other (not checked).
+ */
+int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+            void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
+            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace bytes fa2_bwd needs: lse * log2(e) for the B*H*Lq query rows and,
+ * from the next 256-byte boundary, D = rowsum(dout * o) for the same rows, both
+ * fp32.  Returns 0 for sizes that do not fit.
+ */
+size_t fa2_bwd_workspace_bytes(int B, int H, int Lq);
 
 /* Static English text for a status code (never NULL). */
 const char *fa2_status_string(int status);

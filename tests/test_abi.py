@@ -22,7 +22,8 @@ def header_functions():
 def test_header_declares_the_entry_points():
     assert header_functions() == sorted(["fa2_fwd", "fa2_fwd_f32", "fa2_status_string", "fa2_check_args",
                                          "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
-                                         "fa2_splitkv_num_splits", "fa2_merge_partials"])
+                                         "fa2_splitkv_num_splits", "fa2_merge_partials",
+                                         "fa2_bwd", "fa2_bwd_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -127,3 +128,38 @@ def test_merge_rejects_before_touching_the_device():
     assert f(A, A, 2, 0, 64, A, A, None) == 2
     assert f(A, A, 2, 10, 96, A, A, None) == 3
     assert f(A, A + 4, 2, 10, 64, A, A, None) == 5
+
+
+def test_bwd_rejects_before_touching_the_device():
+    """fa2_bwd refuses bad pointers, sizes and workspaces before any HIP call."""
+    f = fa.lib().fa2_bwd
+    big = 1 << 30
+    args = lambda **kw: [kw.get(n, A) for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv")]
+    assert f(*args(do=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
+    assert f(*args(dk=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
+    assert f(*args(q=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
+    assert f(*args(), 1, 1, 8, 8, 96, 0.1, 0, A, big, None) == 3
+    assert f(*args(), 1, 1, 0, 8, 64, 0.1, 0, A, big, None) == 2
+    assert f(*args(), 1, 1, 8, 8, 64, 0.1, 2, A, big, None) == 4
+    assert f(*args(dv=A + 2), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 5
+    assert f(*args(), 1, 1, 8, 8, 64, 0.1, 0, None, big, None) == 8
+    assert f(*args(), 1, 1, 8, 8, 64, 0.1, 0, A + 8, big, None) == 5
+    need = fa.fa2_bwd_workspace_bytes(1, 1, 8)
+    assert f(*args(), 1, 1, 8, 8, 64, 0.1, 0, A, need - 1, None) == 8
+
+
+def test_bwd_workspace_bytes():
+    """lse * log2(e) for every query row, padded to 256 bytes, then D for every row (fp32)."""
+    for (B, H, Lq) in [(1, 1, 1), (2, 3, 100), (4, 16, 2048)]:
+        rows = B * H * Lq
+        assert fa.fa2_bwd_workspace_bytes(B, H, Lq) == -(-rows * 4 // 256) * 256 + rows * 4
+    assert fa.fa2_bwd_workspace_bytes(0, 1, 8) == 0
+    assert fa.fa2_bwd_workspace_bytes(1, 1, -3) == 0
+
+
+def test_backward_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, q, lse, q)
