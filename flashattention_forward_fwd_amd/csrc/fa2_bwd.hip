@@ -13,10 +13,11 @@
 // Three kernels, enqueued in order on one stream, no atomics (run-to-run
 // bitwise identical results):
 //  1. prep: per row, D_i and lse_i * log2(e) into the caller's workspace.
-//  2. dK/dV: one work-group per block of 128 keys of one (batch, head); each
-//     wavefront keeps K and V of its 32 keys in registers and accumulates dK^T
-//     and dV^T of those keys while 32-row tiles of Q and dO (and their D and
-//     lse) stream through LDS.  Under the causal mask only the query tiles at
+//  2. dK/dV: one work-group per block of 128 keys of one (batch, head); for
+//     each group of 32 keys one wavefront (K in registers) computes P and
+//     accumulates dV^T, another (V in registers) takes that P through LDS one
+//     step later and accumulates dK^T, while 64-row tiles of Q and dO (and
+//     their D and lse) stream through LDS.  Under the causal mask only the query tiles at
 //     or below the block's first key are visited.
 //  3. dQ: one work-group per tile of 128 query rows, laid out like the forward
 //     kernel: each wavefront keeps Q and dO of its 32 rows in registers and
@@ -53,7 +54,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 
 constexpr int kKeysPerWave = 32;                  // dK/dV: keys owned by one wavefront
 constexpr int kKeyBlock = kWaves * kKeysPerWave;  // dK/dV: keys per work-group
-constexpr int kRowTile = 32;                      // dK/dV: query rows per LDS tile
+constexpr int kRowTile = 64;                      // dK/dV: query rows per LDS tile
 
 // A row-major bf16 tile [rows][D] in LDS, its 16-byte chunks XOR-swizzled by
 // row.  The swizzle serves both read patterns the backward uses:
@@ -83,15 +84,15 @@ template <int D> struct BTile {
 // BTile).  Rows past the end of the buffer range arrive as zeros.  Transfer b
 // moves 1 KiB: lane l lands at byte 16 l, i.e. row b * rows_per_xfer + l / chunks
 // and physical chunk l % chunks, and reads that row's logical chunk.
-template <int D, int ROWS>
+template <int D, int ROWS, int NWAVES = kWaves>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t src, int row0, uint16_t *dst, int wave, int lane)
 {
     using T = BTile<D>;
     constexpr int kXfers = ROWS * T::kRowBytes / 1024;
-    static_assert(kXfers % kWaves == 0, "tile must split evenly over the wavefronts");
+    static_assert(kXfers % NWAVES == 0, "tile must split evenly over the wavefronts");
 #pragma unroll
-    for (int x = 0; x < kXfers / kWaves; ++x) {
-        const int b = wave * (kXfers / kWaves) + x;
+    for (int x = 0; x < kXfers / NWAVES; ++x) {
+        const int b = wave * (kXfers / NWAVES) + x;
         const int r = b * T::kRowsPerXfer + lane / T::kChunks;
         const int phys = lane % T::kChunks;
         // The whole offset goes in the VGPR operand, which the range check covers.
@@ -180,8 +181,22 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
 // Work-group id -> (batch*head, key block).  Under the causal mask the first
 // key block sees the most query tiles, so blocks run from the first to the last
 // across all heads (longest first); heads are the fast index.
+//
+// Eight wavefronts, two per SIMD.  For each group of 32 keys, wavefront g
+// (0-3) computes S = Q K^T and P for query tile t, accumulates dV^T += dO^T P,
+// and leaves P (bf16) in LDS; wavefront 4 + g takes that P one step later,
+// computes dP = dO V^T and dS = P (dP - D) for tile t - 1 and accumulates
+// dK^T += Q^T dS.  Each wavefront then holds one 32-key x d accumulator and one
+// of K, V (about 160-190 registers, so two share a SIMD); holding both
+// accumulators in one wavefront needs about 400 and leaves one wavefront per
+// SIMD with nothing to hide its latencies.  The one-step lag keeps a single
+// barrier per step: Q/dO tiles are triple-buffered (t + 1 loading, t read by
+// the dV wavefronts, t - 1 by the dK wavefronts) and P double-buffered.
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvThreads = kDkdvWaves * kWave;
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dkdv_kernel(BwdParams p)
 {
     using T = BTile<D>;
@@ -190,25 +205,33 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     constexpr int kTileElems = kRowTile * D;
     __shared__ __attribute__((aligned(1024))) uint16_t sQ0[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sQ1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ2[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sO0[kTileElems];   // dO tiles
     __shared__ __attribute__((aligned(1024))) uint16_t sO1[kTileElems];
-    // per buffer: lse2 of 64 rows (first 32 used), then D of 64 rows
+    __shared__ __attribute__((aligned(1024))) uint16_t sO2[kTileElems];
+    // P of one tile: [key group][chunk c][lane] x 16 bytes, in the lane order of the B operand
+    __shared__ __attribute__((aligned(1024))) bf16x8 sP0[kWaves * 4 * kWave];
+    __shared__ __attribute__((aligned(1024))) bf16x8 sP1[kWaves * 4 * kWave];
+    // per buffer: lse2 of the tile's 64 rows, then their D
     __shared__ __attribute__((aligned(256))) float sStat0[128];
     __shared__ __attribute__((aligned(256))) float sStat1[128];
+    __shared__ __attribute__((aligned(256))) float sStat2[128];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = tid % kWave;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
+    const bool is_dk = wave >= kWaves;              // wave-uniform role
+    const int grp = wave % kWaves;                  // 32-key group
 
     const int n_bh = p.B * p.H;
     const int bh = blockIdx.x % n_bh;
     const int kb = blockIdx.x / n_bh;
-    const int kw0 = kb * kKeyBlock + wave * kKeysPerWave;   // first key of this wavefront
+    const int kw0 = kb * kKeyBlock + grp * kKeysPerWave;   // first key of this wavefront
     const int key = kw0 + l32;                              // this lane's key
     const int n_qt = (p.Lq + kRowTile - 1) / kRowTile;
-    // Query tiles [t0, n_qt) of the work-group; this wavefront computes from wt0.
+    // Query tiles [t0, n_qt) of the work-group; this key group's start at wt0.
     const int t0 = CAUSAL ? min(kb * (kKeyBlock / kRowTile), n_qt) : 0;
     const int wt0 = CAUSAL ? min(kw0 / kRowTile, n_qt) : 0;
 
@@ -222,101 +245,138 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.delta + row_off), 0, p.Lq * 4, kRawBufferFlags);
 
-    // Tile t: Q and dO rows into the buffers of parity (t - t0), lse2 (wave 0)
-    // and D (wave 1) of rows 32t .. 32t + 63 into the stats buffer.
-    auto load = [&](int t, uint16_t *q_dst, uint16_t *o_dst, float *st_dst) {
-        load_tile<D, kRowTile>(rQ, t * kRowTile, q_dst, wave, lane);
-        load_tile<D, kRowTile>(rO, t * kRowTile, o_dst, wave, lane);
+    // Tile t lives in buffer set (t - t0) % 3: Q, dO, and lse2 (loaded by wave 0)
+    // and D (wave 1) of its 64 rows.
+    auto qbuf = [&](int slot) { return slot == 0 ? sQ0 : slot == 1 ? sQ1 : sQ2; };
+    auto obuf = [&](int slot) { return slot == 0 ? sO0 : slot == 1 ? sO1 : sO2; };
+    auto sbuf = [&](int slot) { return slot == 0 ? sStat0 : slot == 1 ? sStat1 : sStat2; };
+    auto load = [&](int t) {
+        const int slot = (t - t0) % 3;
+        load_tile<D, kRowTile, kDkdvWaves>(rQ, t * kRowTile, qbuf(slot), wave, lane);
+        load_tile<D, kRowTile, kDkdvWaves>(rO, t * kRowTile, obuf(slot), wave, lane);
         if (wave < 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rL : rD, (LDS_AS void *)(st_dst + 64 * wave), 4,
-                                                     4 * (t * kRowTile + lane), 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rL : rD, (LDS_AS void *)(sbuf(slot) + 64 * wave),
+                                                     4, 4 * (t * kRowTile + lane), 0, 0, 0);
     };
-    if (t0 < n_qt) load(t0, sQ0, sO0, sStat0);
+    if (t0 < n_qt) load(t0);
 
-    // K and V of this lane's key as B operands (d chunk 16c + 8hh); zero past Lk.
-    const uint16_t *Kr = static_cast<const uint16_t *>(p.k) + ((size_t)bh * p.Lk + key) * D;
-    const uint16_t *Vr = static_cast<const uint16_t *>(p.v) + ((size_t)bh * p.Lk + key) * D;
-    bf16x8 kf[kDc], vf[kDc];
+    // K (dV wavefronts) or V (dK wavefronts) of this lane's key as B operands
+    // (d chunk 16c + 8hh); zero past Lk.
+    const uint16_t *Xr = static_cast<const uint16_t *>(is_dk ? p.v : p.k) + ((size_t)bh * p.Lk + key) * D;
+    bf16x8 xf[kDc];
 #pragma unroll
-    for (int c = 0; c < kDc; ++c) {
-        kf[c] = load_row_chunk(Kr + 16 * c + 8 * hh, key < p.Lk);
-        vf[c] = load_row_chunk(Vr + 16 * c + 8 * hh, key < p.Lk);
-    }
+    for (int c = 0; c < kDc; ++c)
+        xf[c] = load_row_chunk(Xr + 16 * c + 8 * hh, key < p.Lk);
 
-    f32x16 acc_dk[kDt], acc_dv[kDt];
+    f32x16 acc[kDt];                       // dV^T (wavefronts 0-3) or dK^T (4-7)
 #pragma unroll
-    for (int t = 0; t < kDt; ++t) {
-        acc_dk[t] = f32x16{};
-        acc_dv[t] = f32x16{};
-    }
+    for (int t = 0; t < kDt; ++t)
+        acc[t] = f32x16{};
     const float c2 = p.scale_log2;
 
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int t = t0; t < n_qt; ++t) {
-        const bool odd = (t - t0) & 1;
-        if (t + 1 < n_qt) {
-            if (odd) load(t + 1, sQ0, sO0, sStat0);
-            else     load(t + 1, sQ1, sO1, sStat1);
-        }
-        const LDS_AS char *qb = (const LDS_AS char *)(odd ? sQ1 : sQ0);
-        const LDS_AS char *ob = (const LDS_AS char *)(odd ? sO1 : sO0);
-        const LDS_AS float *st = (const LDS_AS float *)(odd ? sStat1 : sStat0);
-        if (t >= wt0) {
-            // S = Q K^T and dP = dO V^T for 32 rows x this wavefront's 32 keys.
-            f32x16 s = f32x16{}, dp = f32x16{};
+    // Step t: the dV wavefronts work on tile t, the dK wavefronts on tile t - 1.
+    for (int t = t0; t <= n_qt; ++t) {
+        if (t + 1 < n_qt) load(t + 1);
+        if (!is_dk) {
+            if (t < n_qt && t >= wt0) {
+                const int slot = (t - t0) % 3;
+                const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
+                const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
+                const LDS_AS float *st = (const LDS_AS float *)sbuf(slot);
+                // S = Q K^T for 64 rows (two 32-row halves h) x this group's 32
+                // keys.  Entry i of half h is row 32h + 8(i/4) + 4hh + i%4.
+                f32x16 s[2];
 #pragma unroll
-            for (int c = 0; c < kDc; ++c)
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(qb, l32, c, hh), kf[c], s, 0, 0, 0);
+                for (int h = 0; h < 2; ++h) {
+                    s[h] = f32x16{};
 #pragma unroll
-            for (int c = 0; c < kDc; ++c)
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(ob, l32, c, hh), vf[c], dp, 0, 0, 0);
-            // Entry i of the accumulators is row 8(i/4) + 4hh + i%4 of the tile.
-            f32x4 l4[4], d4[4];
+                    for (int c = 0; c < kDc; ++c)
+                        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(qb, 32 * h + l32, c, hh),
+                                                                       xf[c], s[h], 0, 0, 0);
+                }
+                const bool diag = CAUSAL && t == wt0;   // rows of this tile before a key mask it
+                // Chunk c (B operand of the products over the tile's rows) holds
+                // rows 16c + 8(e/4) + 4hh + e%4, e = 0..7: entries 8(c%2) + e of half c/2.
+                LDS_AS bf16x8 *pdst = (LDS_AS bf16x8 *)((t & 1) ? sP1 : sP0) + grp * 4 * kWave;
+                bf16x8 pf[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                l4[g] = *reinterpret_cast<const LDS_AS f32x4 *>(st + 8 * g + 4 * hh);
-                d4[g] = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 8 * g + 4 * hh);
-            }
-            const bool diag = CAUSAL && t == wt0;   // rows of this tile before a key mask it
-            bf16x8 pf[2], dsf[2];
+                for (int c = 0; c < 4; ++c) {
+                    const int h = c >> 1, i0 = 8 * (c & 1);
+                    const f32x4 l4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 4 * hh);
+                    const f32x4 l4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 8 + 4 * hh);
+                    f32x8 v8;
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                f32x8 p8, ds8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int i = 8 * c + e;
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l4[i / 4][i % 4]));
-                    if (diag) {
-                        const int row = t * kRowTile + 8 * (i / 4) + 4 * hh + (i % 4);
-                        pv = key > row ? 0.f : pv;
+                    for (int e = 0; e < 8; ++e) {
+                        const float l2 = e < 4 ? l4a[e] : l4b[e - 4];
+                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i0 + e], c2, -l2));
+                        if (diag) {
+                            const int row = t * kRowTile + 16 * c + 8 * (e / 4) + 4 * hh + (e % 4);
+                            pv = key > row ? 0.f : pv;
+                        }
+                        v8[e] = pv;
                     }
-                    p8[e] = pv;
-                    ds8[e] = pv * (dp[i] - d4[i / 4][i % 4]);
+                    pf[c] = __builtin_convertvector(v8, bf16x8);
+                    pdst[c * kWave + lane] = pf[c];
                 }
-                pf[c] = __builtin_convertvector(p8, bf16x8);
-                dsf[c] = __builtin_convertvector(ds8, bf16x8);
+                // dV^T += dO^T P (contraction over the tile's rows).
+#pragma unroll
+                for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(ob, dt, c, lane), pf[c],
+                                                                          acc[dt], 0, 0, 0);
             }
-            // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's rows).
+        } else {
+            const int tk = t - 1;
+            if (tk >= wt0 && tk >= t0) {
+                const int slot = (tk - t0) % 3;
+                const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
+                const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
+                const LDS_AS float *st = (const LDS_AS float *)sbuf(slot);
+                // dP = dO V^T, same layout as S.
+                f32x16 dp[2];
 #pragma unroll
-            for (int dt = 0; dt < kDt; ++dt)
+                for (int h = 0; h < 2; ++h) {
+                    dp[h] = f32x16{};
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    acc_dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(ob, dt, c, lane), pf[c],
-                                                                         acc_dv[dt], 0, 0, 0);
-                    acc_dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(qb, dt, c, lane), dsf[c],
-                                                                         acc_dk[dt], 0, 0, 0);
+                    for (int c = 0; c < kDc; ++c)
+                        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(ob, 32 * h + l32, c, hh),
+                                                                        xf[c], dp[h], 0, 0, 0);
                 }
+                const LDS_AS bf16x8 *psrc = (const LDS_AS bf16x8 *)((tk & 1) ? sP1 : sP0) + grp * 4 * kWave;
+                bf16x8 dsf[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int h = c >> 1, i0 = 8 * (c & 1);
+                    const bf16x8 pc = psrc[c * kWave + lane];
+                    const f32x4 d4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 4 * hh);
+                    const f32x4 d4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 8 + 4 * hh);
+                    f32x8 v8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)   // dS = P (dP - D)
+                        v8[e] = (float)pc[e] * (dp[h][i0 + e] - (e < 4 ? d4a[e] : d4b[e - 4]));
+                    dsf[c] = __builtin_convertvector(v8, bf16x8);
+                }
+                // dK^T += Q^T dS (contraction over the tile's rows).
+#pragma unroll
+                for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(qb, dt, c, lane), dsf[c],
+                                                                          acc[dt], 0, 0, 0);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads of tile t+1 have landed
-        __syncthreads();                      // ... everyone's, and tile t's buffers are free
+        __syncthreads();                      // ... everyone's; P of tile t is visible; old buffers free
     }
 
     if (key >= p.Lk) return;
     const size_t kv_row = (size_t)bh * p.Lk + key;
-    store_tokens<D>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc_dk, p.scale, hh);
-    store_tokens<D>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc_dv, 1.0f, hh);
+    if (is_dk) store_tokens<D>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc, p.scale, hh);
+    else       store_tokens<D>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc, 1.0f, hh);
 }
 
 // ---------------------------------------------------------------- 3. dQ
@@ -460,8 +520,8 @@ hipError_t launch_bwd_d(const BwdParams &p, bool causal, int64_t rows, const voi
     BwdParams pk = p;
     pk.n_blocks = (p.Lk + kKeyBlock - 1) / kKeyBlock;
     pk.n_wg = pk.n_blocks * p.B * p.H;
-    if (causal) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true>), dim3(pk.n_wg), dim3(kThreads), 0, stream, pk);
-    else        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false>), dim3(pk.n_wg), dim3(kThreads), 0, stream, pk);
+    if (causal) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+    else        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
     BwdParams pq = p;
     pq.n_blocks = (p.Lq + kBr - 1) / kBr;
     pq.n_wg = pq.n_blocks * p.B * p.H;
