@@ -15,6 +15,8 @@ Three references, each a plain reading of the pages:
   (Q blocks outside, K/V blocks inside, running m and l, unnormalised output, one
   division at the end, logsumexp), used to show on the CPU that the tiled method
   reaches the definition's result.
+* ``attention_window_f64`` -- the definition restricted to a window of keys around
+  each query (sliding-window / local attention), computed by ``attn_window_ref.c``.
 * ``attention_bwd_f64`` -- the gradients dQ, dK, dV of the definition (the
   backward pass), by the chain rule, computed by ``attn_bwd_ref.c``.
 * ``merge_partials`` -- the combine of attention results over disjoint key sets
@@ -41,6 +43,14 @@ def _lib():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
             ctypes.c_double, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.oracle_attention_window_f64.restype = ctypes.c_int
+        lib.oracle_attention_window_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
@@ -104,6 +114,38 @@ def attention_f64(q, k, v, scale, causal, rows=None, nthreads=None):
         o.ctypes.data, lse.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attention_f64 rejected its arguments (code %d)" % rc)
+    return o, lse
+
+
+def attention_window_f64(q, k, v, scale, window_left, window_right, rows=None, nthreads=None):
+    """Exact attention in float64 over a window of keys around each query.
+
+    Key j is visible to query i iff (window_left < 0 or j >= i - window_left) and
+    (window_right < 0 or j <= i + window_right); (-1, -1) is full attention and
+    (-1, 0) the causal mask.  Rows that see no key get O = 0 and lse = -inf.
+    Sliding-window attention is the variant "Flash Attention 全解析（上）" section
+    5.3 names; the pages give no formula (the window above is this project's reading).
+    Arguments and results otherwise as ``attention_f64``.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    assert k.shape == (B, H, Lk, d) and v.shape == (B, H, Lk, d)
+    rows_arr = _index_rows(rows, B * H)
+    nr = Lq if rows_arr is None else rows_arr.shape[1]
+    o = np.empty((B, H, nr, d))
+    lse = np.empty((B, H, nr))
+    if nthreads is None:
+        nthreads = default_threads()
+    rc = _lib().oracle_attention_window_f64(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, B, H, Lq, Lk, d, float(scale),
+        int(window_left), int(window_right),
+        rows_arr.ctypes.data if rows_arr is not None else None, nr,
+        o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attention_window_f64 rejected its arguments (code %d)" % rc)
     return o, lse
 
 
