@@ -136,6 +136,10 @@ def main():
                     help="query rows per (batch, head) for the oracle timing (0: every row)")
     ap.add_argument("--splits", type=int, default=None, metavar="S",
                     help="time the split-KV path with S K/V ranges (0: the library's choice)")
+    ap.add_argument("--window", default=None, metavar="WL,WR",
+                    help="time the sliding-window forward fa2_fwd_window (key j visible to query i iff "
+                         "i-WL <= j <= i+WR; negative: unbounded) on a bf16 workload; the window "
+                         "replaces the workload's causal flag")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass fa2_bwd (bf16 workloads) instead of the forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -168,7 +172,25 @@ def main():
     args_common = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal))
     split_info = None
     bwd_info = None
-    if args.backward:
+    win_info = None
+    flops_override = None
+    if args.window is not None:
+        if w.dtype != "bf16" or args.splits is not None or args.backward:
+            print("bench.py: --window takes a bf16 workload, without --splits or --backward",
+                  file=sys.stderr)
+            sys.exit(2)
+        import numpy as np
+        wl, wr = (int(x) for x in args.window.split(","))
+        i = np.arange(w.Lq, dtype=np.int64)
+        lo = np.maximum(0, i - wl) if wl >= 0 else np.zeros_like(i)
+        hi = np.minimum(w.Lk, i + wr + 1) if wr >= 0 else np.full_like(i, w.Lk)
+        pairs = int(np.maximum(hi - lo, 0).sum())
+        flops_override = 4.0 * w.B * w.H * w.d * pairs
+        fn = fa.fa2_fwd_window
+        call = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, wl, wr, stream.cuda_stream)
+        win_info = {"window_left": wl, "window_right": wr, "visible_pairs_per_head": pairs,
+                    "flops_count": "4*d per visible (query, key) pair"}
+    elif args.backward:
         if w.dtype != "bf16" or args.splits is not None:
             print("bench.py: --backward takes a bf16 workload and no --splits", file=sys.stderr)
             sys.exit(2)
@@ -221,10 +243,10 @@ def main():
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     avg_launch_ms = sum(launch_ms) / K
 
-    flops = w.flops * (2.5 if bwd_info else 1.0)
+    flops = flops_override if flops_override is not None else w.flops * (2.5 if bwd_info else 1.0)
     value = flops / (ms_step * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    traffic = stored_traffic(w.name) if split_info is None and bwd_info is None else None
+    traffic = stored_traffic(w.name) if split_info is None and bwd_info is None and win_info is None else None
     algo_bytes = (2 if w.dtype == "bf16" else 4) * w.B * w.H * (2 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq
     if bwd_info:
         # reads q, k, v, o, dout, lse; writes dq, dk, dv
@@ -254,11 +276,14 @@ def main():
     }
     if split_info is not None:
         out["config"]["split_kv"] = split_info
+    if win_info is not None:
+        out["config"]["window"] = win_info
+        out["metric"] = "attention fwd TFLOPS (4·d per visible query-key pair) bf16, sliding window"
     if bwd_info is not None:
         out["config"]["backward"] = bwd_info
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do)
-    elif not args.no_cpu_baseline:
+    elif not args.no_cpu_baseline and win_info is None:
         n = args.cpu_rows_per_head if args.cpu_rows_per_head > 0 else w.Lq
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(n, w.Lq))
     print(json.dumps(out), flush=True)

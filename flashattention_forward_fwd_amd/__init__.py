@@ -11,16 +11,17 @@ and the stream.
 import math
 
 from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_workspace_bytes,  # noqa: F401
-                   fa2_check_args, fa2_fwd, fa2_fwd_f32, fa2_fwd_splitkv, fa2_merge_partials,
+                   fa2_check_args, fa2_fwd, fa2_fwd_f32, fa2_fwd_splitkv, fa2_fwd_window, fa2_merge_partials,
                    fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib, status_string)
 
 __all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f32", "fa2_fwd_splitkv",
            "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
-           "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
+           "fa2_fwd_window", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
            "FA2_MAX_SPLITS"]
 
 
-def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, workspace=None):
+def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, workspace=None,
+            window=None):
     """O = softmax(scale * Q K^T [causal]) V and the per-row logsumexp.
 
     q: [B, H, Lq, d], k and v: [B, H, Lk, d], all bf16 or all fp32 CUDA tensors
@@ -31,6 +32,10 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
     split-KV path with that many K/V ranges (0: the library picks).  Its
     workspace is allocated here unless a large enough uint8 device tensor is
     given.
+
+    window (bf16 only): (window_left, window_right) runs ``fa2_fwd_window`` --
+    key j visible to query i iff i - window_left <= j <= i + window_right, a
+    negative bound meaning unbounded; causal must then be False.
     """
     import torch
 
@@ -53,6 +58,12 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     c = int(bool(causal))
+    if window is not None:
+        if q.dtype != torch.bfloat16 or causal or num_splits is not None:
+            raise ValueError("window takes bfloat16 tensors, causal=False and no num_splits")
+        wl, wr = window
+        fa2_fwd_window(q, k, v, out, lse, B, H, Lq, Lk, d, scale, int(wl), int(wr), stream)
+        return out, lse
     if num_splits is not None:
         if q.dtype != torch.bfloat16:
             raise ValueError("the split-KV path takes bfloat16 tensors")

@@ -32,6 +32,7 @@ SIGNATURES = {
     "fa2_splitkv_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "fa2_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fa2_merge_partials": (_I, [_P, _P, _I, _L, _I, _P, _P, _P]),
+    "fa2_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa2_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
 }
@@ -142,3 +143,12 @@ def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, w
 def fa2_bwd_workspace_bytes(B, H, Lq):
     """libfa2 ``fa2_bwd_workspace_bytes``: bytes of backward workspace (0: sizes rejected)."""
     return lib().fa2_bwd_workspace_bytes(int(B), int(H), int(Lq))
+
+
+def fa2_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_right, stream):
+    """libfa2 ``fa2_fwd_window`` (bf16, keys i - window_left .. i + window_right).  Raises FA2Error."""
+    st = lib().fa2_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                              int(B), int(H), int(Lq), int(Lk), int(d), float(scale),
+                              int(window_left), int(window_right), _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_fwd_window")

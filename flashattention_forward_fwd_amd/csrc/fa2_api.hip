@@ -97,6 +97,8 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
         out->n_qtiles = (int)n_qtiles;
         out->n_splits = 1;
         out->n_wg = (int)(n_qtiles * B * H);
+        out->wl = -1;
+        out->wr = causal ? 0 : -1;
     }
     return FA2_OK;
 }
@@ -224,6 +226,22 @@ int fa2_fwd_f32(const float *q, const float *k, const float *v, float *o, float 
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     if (fa2::launch_fwd_f32(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
+                   void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 2, &p);
+    if (st != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    // Negative bounds all mean "unbounded"; keep them as -1.
+    p.wl = window_left < 0 ? -1 : window_left;
+    p.wr = window_right < 0 ? -1 : window_right;
+    if (fa2::launch_fwd_bf16_window(p, d, static_cast<hipStream_t>(stream)) != hipSuccess)
         return FA2_ERR_LAUNCH;
     return FA2_OK;
 }

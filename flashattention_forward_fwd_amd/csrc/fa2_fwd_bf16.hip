@@ -149,16 +149,18 @@ __device__ __forceinline__ void scores(const LDS_AS char *kb, const bf16x8 (&qf)
     }
 }
 
-// Keys past Lk, and (causal) keys after the lane's query, get -inf.
-template <bool CAUSAL>
-__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int k0, int Lk, int qrow, int hh)
+// Keys past Lk, (causal) keys after the lane's query and (window) keys outside
+// [qrow - wl, qrow + wr] get -inf.
+template <bool CAUSAL, bool WINDOW>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int k0, int Lk, int qrow, int hh, int wl, int wr)
 {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
-            const bool hidden = key >= Lk || (CAUSAL && key > qrow);
+            bool hidden = key >= Lk || (CAUSAL && key > qrow);
+            if (WINDOW) hidden = hidden || (wl >= 0 && key < qrow - wl) || (wr >= 0 && key > qrow + wr);
             s[t][i] = hidden ? -INFINITY : s[t][i];
         }
 }
@@ -253,12 +255,12 @@ __device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, f
 // One step of the pipelined loop for tile j: probabilities of tile j (VALU)
 // while the scores of tile j+1 run (MFMA), then O~ += P~_j V_j (MFMA) while the
 // max of tile j+1 is taken (VALU).
-template <int D, bool CAUSAL, bool EMPTY_ROWS>
+template <int D, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW>
 __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const LDS_AS char *v_cur,
                                                const bf16x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
                                                f32x16 (&s_cur)[2], float &m, float &lpart, float &alpha,
-                                               float c2, int j, int t0, int n_plain, int Lk, int qrow,
-                                               int hh, int k_lane, int v_lane)
+                                               float c2, int j, int t0, int plain_lo, int n_plain, int Lk,
+                                               int qrow, int hh, int k_lane, int v_lane, int wl, int wr)
 {
     if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
     bf16x8 pf[4];
@@ -272,9 +274,10 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
     // letting it sink past the branch where nothing overlaps it.
     asm volatile("" ::"v"(rs), "v"(mt));
     lpart += rs;
-    // Tiles on the causal diagonal or the key tail (few): mask, take the max again.
-    if (j + 1 >= n_plain) {
-        mask_scores<CAUSAL>(s_next, (t0 + j + 1) * kBc, Lk, qrow, hh);
+    // Tiles on the causal diagonal, a window edge or the key tail (few): mask,
+    // take the max again.
+    if (j + 1 >= n_plain || (WINDOW && j + 1 < plain_lo)) {
+        mask_scores<CAUSAL, WINDOW>(s_next, (t0 + j + 1) * kBc, Lk, qrow, hh, wl, wr);
         mt = row_max_scaled(s_next, c2);
     }
     alpha = update_max<EMPTY_ROWS>(m, mt);
@@ -286,13 +289,19 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
 // query tile's K/V tiles and writes the fp32 partial O (normalised by its own
 // row sum) and partial LSE of that range; rows that see no key of the range
 // get LSE = -inf and no O.  Otherwise it covers all tiles and writes bf16 O.
-template <int D, bool CAUSAL, bool SPLIT>
+// WINDOW (with CAUSAL and SPLIT false): key j is visible to query i iff
+// (p.wl < 0 or j >= i - p.wl) and (p.wr < 0 or j <= i + p.wr); the work-group
+// visits only the tiles that hold a key visible to one of its rows, and a row
+// that sees no key gets O = 0 and LSE = -inf.
+template <int D, bool CAUSAL, bool SPLIT, bool WINDOW = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
 {
     using T = Tile<D>;
-    // Only a causal range that starts after tile 0 can hold rows without a visible key.
-    constexpr bool kEmptyRows = SPLIT && CAUSAL;
+    static_assert(!WINDOW || (!CAUSAL && !SPLIT), "the window replaces the causal mask; no split");
+    // Rows without a visible key in a visited tile range: a causal range that
+    // starts after tile 0, or a window (rows at a window edge of the block).
+    constexpr bool kEmptyRows = (SPLIT && CAUSAL) || WINDOW;
     constexpr int kDc = D / 16;          // 16-wide d chunks of the QK^T product
     constexpr int kDt = D / 32;          // 32-row d tiles of the output
     // Tile t of K lives in sK0 / sK1 by the parity of t, same for V.  Four
@@ -319,8 +328,21 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     }
     const int n_kv_all = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
     // This work-group's K/V tiles: [t0, t0 + n_kv).
-    const int t0 = SPLIT ? (int)((int64_t)split * n_kv_all / p.n_splits) : 0;
-    const int n_kv = SPLIT ? (int)((int64_t)(split + 1) * n_kv_all / p.n_splits) - t0 : n_kv_all;
+    int t0 = SPLIT ? (int)((int64_t)split * n_kv_all / p.n_splits) : 0;
+    int n_kv = SPLIT ? (int)((int64_t)(split + 1) * n_kv_all / p.n_splits) - t0 : n_kv_all;
+    if (WINDOW) {
+        // Keys visible to some row of the block: [key_lo, key_hi).
+        const int q_first = qt * kBr;
+        const int q_last = min(q_first + kBr - 1, p.Lq - 1);
+        const int64_t key_lo = p.wl < 0 ? 0 : max((int64_t)0, (int64_t)q_first - p.wl);
+        const int64_t key_hi = p.wr < 0 ? p.Lk : min((int64_t)p.Lk, (int64_t)q_last + p.wr + 1);
+        t0 = 0;
+        n_kv = 0;
+        if (key_hi > key_lo) {
+            t0 = (int)(key_lo / kBc);
+            n_kv = (int)((key_hi + kBc - 1) / kBc) - t0;
+        }
+    }
     // Partial-result row of (split, bh, query 0 of this head).
     const size_t part_row0 = ((size_t)split * p.B * p.H + bh) * p.Lq;
     if (SPLIT && n_kv == 0) {                 // empty range: every row is empty
@@ -344,9 +366,24 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     // Tiles this wavefront computes, counted from t0: [0, n_plain) need no mask,
     // [n_plain, n_wave) cross the causal diagonal or the end of the keys; the
     // work-group's other tiles are masked for all of its rows (it only helps
-    // load them).
-    int n_wave = 0, n_plain = 0;
-    if (wave_active) {
+    // load them).  Window: [plain_lo, n_plain) need no mask, the tiles before
+    // plain_lo cross the left edge of some row's window.
+    int n_wave = 0, n_plain = 0, plain_lo = 0;
+    if (WINDOW) {
+        if (wave_active) {
+            const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
+            int end = t0 + n_kv;
+            if (p.wr >= 0) end = (int)min((int64_t)end, ((int64_t)wave_qlast + p.wr) / kBc + 1);
+            n_wave = max(end - t0, 0);
+            // A tile needs no mask when the window of every row of the wave holds it.
+            const int64_t left = p.wl < 0 ? 0 : (int64_t)wave_qlast - p.wl;     // last row's left edge
+            const int64_t first_plain = left <= 0 ? 0 : (left + kBc - 1) / kBc;
+            int64_t end_plain = p.Lk / kBc;
+            if (p.wr >= 0) end_plain = min(end_plain, ((int64_t)q0 + p.wr + 1) / kBc);
+            plain_lo = (int)min(max(first_plain - t0, (int64_t)0), (int64_t)n_wave);
+            n_plain = (int)min(max(end_plain - t0, (int64_t)0), (int64_t)n_wave);
+        }
+    } else if (wave_active) {
         const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
         const int end = CAUSAL ? min(t0 + n_kv, wave_qlast / kBc + 1) : t0 + n_kv;
         int plain = min(end, p.Lk / kBc);
@@ -399,7 +436,8 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     f32x16 s_cur[2];
     if (n_wave > 0) {
         scores<D>((const LDS_AS char *)sK0, qf, s_cur, k_lane);
-        if (n_plain == 0) mask_scores<CAUSAL>(s_cur, t0 * kBc, p.Lk, qrow, hh);
+        if (n_plain == 0 || (WINDOW && plain_lo > 0))
+            mask_scores<CAUSAL, WINDOW>(s_cur, t0 * kBc, p.Lk, qrow, hh, p.wl, p.wr);
         m = row_max_scaled(s_cur, c2);
     }
     __syncthreads();                          // sK0 may now be refilled
@@ -411,18 +449,18 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         // even tile j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK0, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
-        pipelined_step<D, CAUSAL, kEmptyRows>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o,
-                                              s_cur, m, lpart, alpha, c2, j, t0, n_plain, p.Lk, qrow, hh,
-                                              k_lane, v_lane);
+        pipelined_step<D, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf,
+                                                      acc_o, s_cur, m, lpart, alpha, c2, j, t0, plain_lo, n_plain,
+                                                      p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
         __syncthreads();                      // ... everyone's, and the read buffers are free
         if (++j + 1 >= n_wave) break;
         // odd tile j: K_{j+1} in sK0, V_j in sV1; loads K_{j+2} -> sK1, V_{j+1} -> sV0
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK1, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
-        pipelined_step<D, CAUSAL, kEmptyRows>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o,
-                                              s_cur, m, lpart, alpha, c2, j, t0, n_plain, p.Lk, qrow, hh,
-                                              k_lane, v_lane);
+        pipelined_step<D, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf,
+                                                      acc_o, s_cur, m, lpart, alpha, c2, j, t0, plain_lo, n_plain,
+                                                      p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         ++j;
@@ -468,7 +506,9 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         if (hh == 0) p.lse[part_row0 + qrow] = lse;
         return;
     }
-    const float inv_l = 1.0f / l;
+    // A window can leave a row without a visible key: O = 0, LSE = -inf.
+    const bool seen = !WINDOW || l > 0.0f;
+    const float inv_l = seen ? 1.0f / l : 0.0f;
     uint16_t *O = static_cast<uint16_t *>(p.o) + ((size_t)bh * p.Lq + qrow) * D;
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
@@ -507,6 +547,14 @@ hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t s
 hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
     return launch<true>(p, d, causal, stream);
+}
+
+hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
+{
+    const dim3 grid(p.n_wg), block(kThreads);
+    if (d == 64) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, false, false, true>), grid, block, 0, stream, p);
+    else         hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, false, false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace fa2

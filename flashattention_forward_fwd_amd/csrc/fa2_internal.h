@@ -19,6 +19,8 @@ struct FwdParams {
     int n_qtiles;       // ceil(Lq / rows per work-group)
     int n_splits;       // K/V ranges per query tile (1: plain forward)
     int n_wg;           // n_qtiles * B * H * n_splits
+    int wl, wr;         // window kernels: key j visible to query i iff
+                        // (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr)
 };
 
 // Everything a backward kernel needs (q, k, v, dout bf16 inputs; dq, dk, dv bf16
@@ -111,6 +113,8 @@ hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t st
 // Split-KV partials: p.o is the fp32 partial-output array, p.lse the partial
 // logsumexps, both indexed by (split, b*h, row).
 hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream);
+// Window forward: p.wl, p.wr select the visible keys (bf16, one pass).
+hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream);
 // Backward: D and lse2 into p.delta / p.lse2 from o and lse, then dK/dV, then dQ.
 hipError_t launch_bwd_bf16(const BwdParams &p, int d, bool causal, const void *o, const float *lse,
                            hipStream_t stream);

@@ -93,6 +93,24 @@ int fa2_fwd_f32(const float *q, const float *k, const float *v, float *o, float 
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream);
 
 /*
+ * Forward pass over a window of keys around each query (sliding-window / local
+ * attention), bf16: key j is visible to query i iff
+ *     (window_left  < 0  or  j >= i - window_left)   and
+ *     (window_right < 0  or  j <= i + window_right),
+ * so (-1, -1) is full attention, (-1, 0) the causal mask of fa2_fwd, and
+ * (W - 1, 0) a causal window of W keys.  "Flash Attention 全解析（上）", section
+ * 5.3, names sliding-window attention as a variant the family goes on to support;
+ * the pages give no formula, and this window is the reading adopted.  Only the K/V
+ * blocks that hold a visible key of some row of a Q block are visited, so the work
+ * scales with the window, not with Lk.  A row that sees no key (possible only with
+ * a window, e.g. Lq > Lk) gets o = 0 and lse = -inf.  Same arguments, precision,
+ * layout and error rules as fa2_fwd otherwise.
+ */
+int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
+                   void *stream);
+
+/*
  * Split-KV forward (FlashDecoding): the same result as fa2_fwd, computed in two
  * stages on `stream` ("Flash Attention 全解析（上）", section 4.3).
  *

@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     assert header_functions() == sorted(["fa2_fwd", "fa2_fwd_f32", "fa2_status_string", "fa2_check_args",
                                          "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
                                          "fa2_splitkv_num_splits", "fa2_merge_partials",
-                                         "fa2_bwd", "fa2_bwd_workspace_bytes"])
+                                         "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd_window"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -163,3 +163,12 @@ def test_backward_refuses_host_tensors():
     lse = torch.zeros(1, 1, 4)
     with pytest.raises(ValueError):
         fa.backward(q, q, q, q, lse, q)
+
+
+def test_window_rejects_before_touching_the_device():
+    f = fa.lib().fa2_fwd_window
+    assert f(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 4, 0, None) == 1
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 4, 0, None) == 3
+    assert f(A, A, A, A, A, 1, 1, 0, 8, 64, 0.1, 4, 0, None) == 2
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, float("nan"), 4, 0, None) == 4
+    assert f(A, A, A, A, A + 4, 1, 1, 8, 8, 64, 0.1, 4, 0, None) == 5
