@@ -10,13 +10,13 @@ and the stream.
 """
 import math
 
-from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_workspace_bytes,  # noqa: F401
+from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_window, fa2_bwd_workspace_bytes,  # noqa: F401
                    fa2_check_args, fa2_fwd, fa2_fwd_f32, fa2_fwd_splitkv, fa2_fwd_window, fa2_merge_partials,
                    fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib, status_string)
 
 __all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f32", "fa2_fwd_splitkv",
            "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
-           "fa2_fwd_window", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
+           "fa2_fwd_window", "fa2_bwd", "fa2_bwd_window", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
            "FA2_MAX_SPLITS"]
 
 
@@ -107,14 +107,17 @@ def merge_partials(o_parts, lse_parts, out=None, lse=None):
     return out, lse
 
 
-def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None):
+def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
+             window=None):
     """Gradients (dq, dk, dv) of attention for the upstream gradient dout (libfa2 ``fa2_bwd``).
 
     q, k, v, o, dout: bfloat16 CUDA tensors (q, o, dout [B, H, Lq, d]; k, v
     [B, H, Lk, d]), o and lse (fp32 [B, H, Lq]) as returned by ``forward`` for
     the same q, k, v, causal and scale.  Returns bf16 (dq, dk, dv).  The
     workspace is allocated here unless a large enough uint8 device tensor is
-    given.  Enqueued on the current stream.
+    given.  window: (window_left, window_right) of a ``forward(..., window=...)``
+    call runs ``fa2_bwd_window`` (causal must then be False).  Enqueued on the
+    current stream.
     """
     import torch
 
@@ -143,6 +146,12 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), workspace,
-            workspace.numel() * workspace.element_size(), stream)
+    nbytes = workspace.numel() * workspace.element_size()
+    if window is not None:
+        if causal:
+            raise ValueError("window replaces the causal mask; pass causal=False")
+        fa2_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(window[0]), int(window[1]),
+                       workspace, nbytes, stream)
+        return dq, dk, dv
+    fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), workspace, nbytes, stream)
     return dq, dk, dv

@@ -35,6 +35,7 @@ SIGNATURES = {
     "fa2_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa2_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
+    "fa2_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
 }
 
 _lib = None
@@ -152,3 +153,14 @@ def fa2_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_
                               int(window_left), int(window_right), _ptr(stream))
     if st != FA2_OK:
         raise FA2Error(st, "fa2_fwd_window")
+
+
+def fa2_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, window_left, window_right,
+                   workspace, workspace_bytes, stream):
+    """libfa2 ``fa2_bwd_window`` (gradients of fa2_fwd_window).  Raises FA2Error."""
+    st = lib().fa2_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                              _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale),
+                              int(window_left), int(window_right), _ptr(workspace), int(workspace_bytes),
+                              _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_bwd_window")

@@ -192,6 +192,8 @@ int prepare_bwd(const void *q, const void *k, const void *v, const void *o, cons
         out->scale_log2 = (float)((double)scale * 1.4426950408889634074);
         out->n_blocks = 0;
         out->n_wg = 0;
+        out->wl = -1;
+        out->wr = causal ? 0 : -1;
     }
     return FA2_OK;
 }
@@ -333,7 +335,24 @@ int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const fl
                          workspace_bytes_given, &p);
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
-    if (fa2::launch_bwd_bf16(p, d, causal != 0, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (fa2::launch_bwd_bf16(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fa2_bwd_window(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                   void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale,
+                   int window_left, int window_right, void *workspace, size_t workspace_bytes_given,
+                   void *stream)
+{
+    fa2::BwdParams p;
+    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, 0, workspace,
+                         workspace_bytes_given, &p);
+    if (st != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    p.wl = window_left < 0 ? -1 : window_left;
+    p.wr = window_right < 0 ? -1 : window_right;
+    if (fa2::launch_bwd_bf16(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
         return FA2_ERR_LAUNCH;
     return FA2_OK;
 }

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * kWave;
 
-template <int D, bool CAUSAL>
+template <int D, bool MASKED>
 __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dkdv_kernel(BwdParams p)
 {
@@ -230,10 +230,26 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     const int kb = blockIdx.x / n_bh;
     const int kw0 = kb * kKeyBlock + grp * kKeysPerWave;   // first key of this wavefront
     const int key = kw0 + l32;                              // this lane's key
-    const int n_qt = (p.Lq + kRowTile - 1) / kRowTile;
-    // Query tiles [t0, n_qt) of the work-group; this key group's start at wt0.
-    const int t0 = CAUSAL ? min(kb * (kKeyBlock / kRowTile), n_qt) : 0;
-    const int wt0 = CAUSAL ? min(kw0 / kRowTile, n_qt) : 0;
+    // Query tiles [t0, t_end) of the work-group: those holding a query that sees
+    // one of its keys; this key group's own range is [wt0, wt_end).  MASKED: key
+    // j is visible to query i iff (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr),
+    // i.e. i in [j - wr, j + wl].
+    int t0 = 0, t_end = (p.Lq + kRowTile - 1) / kRowTile, wt0 = 0, wt_end = t_end;
+    if (MASKED) {
+        const int64_t k_first = (int64_t)kb * kKeyBlock;
+        const int64_t k_last = min(k_first + kKeyBlock - 1, (int64_t)p.Lk - 1);
+        const int64_t q_lo = p.wr < 0 ? 0 : max((int64_t)0, k_first - p.wr);
+        const int64_t q_hi = p.wl < 0 ? p.Lq : min((int64_t)p.Lq, k_last + p.wl + 1);
+        t0 = t_end = 0;
+        if (q_hi > q_lo) {
+            t0 = (int)(q_lo / kRowTile);
+            t_end = (int)((q_hi + kRowTile - 1) / kRowTile);
+        }
+        const int64_t wq_lo = p.wr < 0 ? 0 : max((int64_t)0, (int64_t)kw0 - p.wr);
+        const int64_t wq_hi = p.wl < 0 ? p.Lq : min((int64_t)p.Lq, (int64_t)kw0 + kKeysPerWave + p.wl);
+        wt0 = max(t0, (int)(wq_lo / kRowTile));
+        wt_end = min(t_end, (int)((wq_hi + kRowTile - 1) / kRowTile));
+    }
 
     const size_t row_off = (size_t)bh * p.Lq;
     const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
@@ -258,7 +274,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rL : rD, (LDS_AS void *)(sbuf(slot) + 64 * wave),
                                                      4, 4 * (t * kRowTile + lane), 0, 0, 0);
     };
-    if (t0 < n_qt) load(t0);
+    if (t0 < t_end) load(t0);
 
     // K (dV wavefronts) or V (dK wavefronts) of this lane's key as B operands
     // (d chunk 16c + 8hh); zero past Lk.
@@ -278,10 +294,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     __syncthreads();
 
     // Step t: the dV wavefronts work on tile t, the dK wavefronts on tile t - 1.
-    for (int t = t0; t <= n_qt; ++t) {
-        if (t + 1 < n_qt) load(t + 1);
+    for (int t = t0; t <= t_end; ++t) {
+        if (t + 1 < t_end) load(t + 1);
         if (!is_dk) {
-            if (t < n_qt && t >= wt0) {
+            if (t >= wt0 && t < wt_end) {
                 const int slot = (t - t0) % 3;
                 const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
                 const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
@@ -297,7 +313,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                         s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(qb, 32 * h + l32, c, hh),
                                                                        xf[c], s[h], 0, 0, 0);
                 }
-                const bool diag = CAUSAL && t == wt0;   // rows of this tile before a key mask it
+                // Does every (row, key) pair of this tile and key group lie in the window?
+                const bool need_mask =
+                    MASKED && !((p.wl < 0 || (int64_t)kw0 >= (int64_t)t * kRowTile + kRowTile - 1 - p.wl) &&
+                                (p.wr < 0 || (int64_t)kw0 + kKeysPerWave - 1 <= (int64_t)t * kRowTile + p.wr));
                 // Chunk c (B operand of the products over the tile's rows) holds
                 // rows 16c + 8(e/4) + 4hh + e%4, e = 0..7: entries 8(c%2) + e of half c/2.
                 LDS_AS bf16x8 *pdst = (LDS_AS bf16x8 *)((t & 1) ? sP1 : sP0) + grp * 4 * kWave;
@@ -312,9 +331,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                     for (int e = 0; e < 8; ++e) {
                         const float l2 = e < 4 ? l4a[e] : l4b[e - 4];
                         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i0 + e], c2, -l2));
-                        if (diag) {
+                        if (need_mask) {
                             const int row = t * kRowTile + 16 * c + 8 * (e / 4) + 4 * hh + (e % 4);
-                            pv = key > row ? 0.f : pv;
+                            const bool hidden = (p.wl >= 0 && key < row - p.wl) || (p.wr >= 0 && key > row + p.wr);
+                            pv = hidden ? 0.f : pv;
                         }
                         v8[e] = pv;
                     }
@@ -331,7 +351,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
             }
         } else {
             const int tk = t - 1;
-            if (tk >= wt0 && tk >= t0) {
+            if (tk >= wt0 && tk < wt_end) {
                 const int slot = (tk - t0) % 3;
                 const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
                 const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
@@ -380,7 +400,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------- 3. dQ
-template <int D, bool CAUSAL>
+template <int D, bool MASKED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_bwd_dq_kernel(BwdParams p)
 {
@@ -401,7 +421,20 @@ void fa2_bwd_dq_kernel(BwdParams p)
 
     int bh, qt;
     map_workgroup(blockIdx.x, p.n_wg, p.n_blocks, bh, qt);
-    const int n_kv = kv_tiles_for(qt, p.Lq, p.Lk, CAUSAL);
+    // K/V tiles [t0, t0 + n_kv) hold a key some row of the block sees (MASKED:
+    // the window of the forward's window kernel; causal is (-1, 0)).
+    int t0 = 0, n_kv = (p.Lk + kBc - 1) / kBc;
+    if (MASKED) {
+        const int q_first = qt * kBr;
+        const int q_last = min(q_first + kBr - 1, p.Lq - 1);
+        const int64_t key_lo = p.wl < 0 ? 0 : max((int64_t)0, (int64_t)q_first - p.wl);
+        const int64_t key_hi = p.wr < 0 ? p.Lk : min((int64_t)p.Lk, (int64_t)q_last + p.wr + 1);
+        n_kv = 0;
+        if (key_hi > key_lo) {
+            t0 = (int)(key_lo / kBc);
+            n_kv = (int)((key_hi + kBc - 1) / kBc) - t0;
+        }
+    }
 
     const size_t kv_off = (size_t)bh * p.Lk * D;
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
@@ -414,20 +447,26 @@ void fa2_bwd_dq_kernel(BwdParams p)
     const bool row_ok = qrow < p.Lq;
     const bool wave_active = q0 < p.Lq;
 
-    // K/V tiles this wavefront computes: [0, n_plain) unmasked, [n_plain, n_wave)
-    // crossing the diagonal or the end of the keys (as in the forward kernel).
-    int n_wave = 0, n_plain = 0;
+    // Tiles this wavefront computes, counted from t0: [0, n_wave); those in
+    // [plain_lo, n_plain) are seen whole by every row of the wavefront, the others
+    // cross a window edge or the end of the keys and are masked per element.
+    int n_wave = 0, n_plain = 0, plain_lo = 0;
     if (wave_active) {
         const int wave_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
-        const int end = CAUSAL ? min(n_kv, wave_qlast / kBc + 1) : n_kv;
-        int plain = p.Lk / kBc;
-        if (CAUSAL) plain = min(plain, (q0 + 1) / kBc);
-        n_wave = end;
-        n_plain = min(plain, n_wave);
+        int64_t end = t0 + n_kv, first_plain = 0, end_plain = p.Lk / kBc;
+        if (MASKED) {
+            if (p.wr >= 0) end = min(end, ((int64_t)wave_qlast + p.wr) / kBc + 1);
+            const int64_t left = p.wl < 0 ? 0 : (int64_t)wave_qlast - p.wl;
+            first_plain = left <= 0 ? 0 : (left + kBc - 1) / kBc;
+            if (p.wr >= 0) end_plain = min(end_plain, ((int64_t)q0 + p.wr + 1) / kBc);
+        }
+        n_wave = (int)max(end - t0, (int64_t)0);
+        plain_lo = (int)min(max(first_plain - t0, (int64_t)0), (int64_t)n_wave);
+        n_plain = (int)min(max(end_plain - t0, (int64_t)0), (int64_t)n_wave);
     }
 
-    load_tile<D, kBc>(rK, 0, sK0, wave, lane);
-    load_tile<D, kBc>(rV, 0, sV0, wave, lane);
+    load_tile<D, kBc>(rK, t0 * kBc, sK0, wave, lane);
+    load_tile<D, kBc>(rV, t0 * kBc, sV0, wave, lane);
 
     const size_t qoff = ((size_t)bh * p.Lq + qrow);
     const uint16_t *Qr = static_cast<const uint16_t *>(p.q) + qoff * D;
@@ -453,8 +492,8 @@ void fa2_bwd_dq_kernel(BwdParams p)
     for (int j = 0; j < n_kv; ++j) {
         const bool odd = j & 1;
         if (j + 1 < n_kv) {
-            load_tile<D, kBc>(rK, (j + 1) * kBc, odd ? sK0 : sK1, wave, lane);
-            load_tile<D, kBc>(rV, (j + 1) * kBc, odd ? sV0 : sV1, wave, lane);
+            load_tile<D, kBc>(rK, (t0 + j + 1) * kBc, odd ? sK0 : sK1, wave, lane);
+            load_tile<D, kBc>(rV, (t0 + j + 1) * kBc, odd ? sV0 : sV1, wave, lane);
         }
         const LDS_AS char *kbuf = (const LDS_AS char *)(odd ? sK1 : sK0);
         const LDS_AS char *vbuf = (const LDS_AS char *)(odd ? sV1 : sV0);
@@ -474,8 +513,8 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(vbuf, 32 * t + l32, c, hh), of[c],
                                                                     dp[t], 0, 0, 0);
             }
-            // Entry i of tile t is key 64j + 32t + 8(i/4) + 4hh + i%4.
-            const bool need_mask = j >= n_plain;
+            // Entry i of tile t is key 64(t0 + j) + 32t + 8(i/4) + 4hh + i%4.
+            const bool need_mask = j < plain_lo || j >= n_plain;
             bf16x8 dsf[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -486,8 +525,10 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     const int i = i0 + e;
                     float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -lse2));
                     if (need_mask) {
-                        const int kk = j * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
-                        pv = (kk >= p.Lk || (CAUSAL && kk > qrow)) ? 0.f : pv;
+                        const int kk = (t0 + j) * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
+                        bool hidden = kk >= p.Lk;
+                        if (MASKED) hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
+                        pv = hidden ? 0.f : pv;
                     }
                     ds8[e] = pv * (dp[t][i] - dlt);
                 }
@@ -510,7 +551,7 @@ void fa2_bwd_dq_kernel(BwdParams p)
 }
 
 template <int D>
-hipError_t launch_bwd_d(const BwdParams &p, bool causal, int64_t rows, const void *o, const float *lse,
+hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const void *o, const float *lse,
                         hipStream_t stream)
 {
     const int64_t threads = rows * (D / 8);
@@ -520,24 +561,24 @@ hipError_t launch_bwd_d(const BwdParams &p, bool causal, int64_t rows, const voi
     BwdParams pk = p;
     pk.n_blocks = (p.Lk + kKeyBlock - 1) / kKeyBlock;
     pk.n_wg = pk.n_blocks * p.B * p.H;
-    if (causal) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+    if (masked) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
     else        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
     BwdParams pq = p;
     pq.n_blocks = (p.Lq + kBr - 1) / kBr;
     pq.n_wg = pq.n_blocks * p.B * p.H;
-    if (causal) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    if (masked) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
     else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams &p, int d, bool causal, const void *o, const float *lse,
-                           hipStream_t stream)
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream)
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
-    return d == 64 ? launch_bwd_d<64>(p, causal, rows, o, lse, stream)
-                   : launch_bwd_d<128>(p, causal, rows, o, lse, stream);
+    const bool masked = p.wl >= 0 || p.wr >= 0;
+    return d == 64 ? launch_bwd_d<64>(p, masked, rows, o, lse, stream)
+                   : launch_bwd_d<128>(p, masked, rows, o, lse, stream);
 }
 
 }  // namespace fa2

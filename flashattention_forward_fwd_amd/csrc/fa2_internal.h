@@ -40,6 +40,8 @@ struct BwdParams {
     float scale_log2;   // scale * log2(e)
     int n_blocks;       // per head: key blocks (dK/dV kernel) or query tiles (dQ kernel)
     int n_wg;           // n_blocks * B * H
+    int wl, wr;         // key j visible to query i iff (wl < 0 or j >= i - wl) and
+                        // (wr < 0 or j <= i + wr); causal is (-1, 0), full (-1, -1)
 };
 
 constexpr int kWave = 64;          // CDNA wavefront width
@@ -115,9 +117,9 @@ hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t st
 hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream);
 // Window forward: p.wl, p.wr select the visible keys (bf16, one pass).
 hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream);
-// Backward: D and lse2 into p.delta / p.lse2 from o and lse, then dK/dV, then dQ.
-hipError_t launch_bwd_bf16(const BwdParams &p, int d, bool causal, const void *o, const float *lse,
-                           hipStream_t stream);
+// Backward: D and lse2 into p.delta / p.lse2 from o and lse, then dK/dV, then dQ,
+// for the keys p.wl / p.wr leave visible.
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                         int d, void *o, float *lse, hipStream_t stream);
 }  // namespace fa2

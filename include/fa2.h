@@ -218,6 +218,16 @@ int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const fl
             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Backward pass of fa2_fwd_window: the gradients of attention over the key
+ * window (window_left, window_right) of fa2_fwd_window, from its o and lse.
+ * Rows that see no key contribute nothing (their o = 0, D = 0, P = 0); keys no
+ * row sees get dk = dv = 0.  Same arguments and rules as fa2_bwd otherwise.
+ */
+int fa2_bwd_window(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                   void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale,
+                   int window_left, int window_right, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Workspace bytes fa2_bwd needs: lse * log2(e) for the B*H*Lq query rows and,
  * from the next 256-byte boundary, D = rowsum(dout * o) for the same rows, both
  * fp32.  Returns 0 for sizes that do not fit.

@@ -25,10 +25,14 @@
  * out (the reading recorded with the others in the design notes).  Nothing is
  * tiled: every row's whole score row is rebuilt, and every key's gradient is a
  * plain sum over the rows that see it.  Parallelism is only across independent
- * items.  Causal visibility is top-left (key j visible to query i iff j <= i),
- * as in the forward reference.
+ * items.
  *
- * oracle_attention_bwd_f64
+ * Visibility: key j is visible to query i iff (wl < 0 or j >= i - wl) and
+ * (wr < 0 or j <= i + wr), the window of the window forward reference; causal
+ * (top-left, j <= i) is (-1, 0) and full attention (-1, -1).  A row that sees no
+ * key has O = 0, contributes nothing and gets dq = 0.
+ *
+ * oracle_attention_bwd_window_f64 / oracle_attention_bwd_f64 (causal 0 or 1)
  *   q, dout [B, H, Lq, d], k, v [B, H, Lk, d]   row-major, double
  *   rows  NULL: dq for every query row; else int64 [B*H, nrows] query indices
  *   keys  NULL: dk, dv for every key;   else int64 [B*H, nkeys] key indices
@@ -46,14 +50,33 @@
 #define ORACLE_ERR_ARG 1
 #define ORACLE_ERR_NOMEM 2
 
-int oracle_attention_bwd_f64(const double *q, const double *k, const double *v, const double *dout,
-                             int B, int H, int Lq, int Lk, int d, double scale, int causal,
-                             const int64_t *rows, int nrows, const int64_t *keys, int nkeys,
-                             double *dq, double *dk, double *dv, int nthreads)
+/* Keys [*lo, *hi) visible to query i. */
+static void keys_of_row(int i, int Lk, int wl, int wr, int *lo, int *hi)
+{
+    int64_t a = 0, b = Lk;
+    if (wl >= 0 && (int64_t)i - wl > a) a = (int64_t)i - wl;
+    if (wr >= 0 && (int64_t)i + wr + 1 < b) b = (int64_t)i + wr + 1;
+    *lo = (int)a;
+    *hi = (int)(b > a ? b : a);
+}
+
+/* Queries [*lo, *hi) that see key j (the same predicate solved for i). */
+static void rows_of_key(int j, int Lq, int wl, int wr, int *lo, int *hi)
+{
+    int64_t a = 0, b = Lq;
+    if (wr >= 0 && (int64_t)j - wr > a) a = (int64_t)j - wr;
+    if (wl >= 0 && (int64_t)j + wl + 1 < b) b = (int64_t)j + wl + 1;
+    *lo = (int)a;
+    *hi = (int)(b > a ? b : a);
+}
+
+int oracle_attention_bwd_window_f64(const double *q, const double *k, const double *v, const double *dout,
+                                    int B, int H, int Lq, int Lk, int d, double scale, int wl, int wr,
+                                    const int64_t *rows, int nrows, const int64_t *keys, int nkeys,
+                                    double *dq, double *dk, double *dv, int nthreads)
 {
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return ORACLE_ERR_ARG;
     if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || d <= 0) return ORACLE_ERR_ARG;
-    if (causal != 0 && causal != 1) return ORACLE_ERR_ARG;
     const int nr = rows ? nrows : Lq;
     const int nk = keys ? nkeys : Lk;
     if (nr <= 0 || nk <= 0) return ORACLE_ERR_ARG;
@@ -106,36 +129,36 @@ int oracle_attention_bwd_f64(const double *q, const double *k, const double *v, 
             const double *doi = dout + ((size_t)bh * Lq + i) * d;
             const double *Kb = k + (size_t)bh * Lk * d;
             const double *Vb = v + (size_t)bh * Lk * d;
-            int nvis = Lk;
-            if (causal && i + 1 < Lk) nvis = i + 1;
-            for (int j = 0; j < nvis; ++j) {
+            int lo, hi;
+            keys_of_row(i, Lk, wl, wr, &lo, &hi);
+            for (int j = lo; j < hi; ++j) {
                 double dot = 0.0, dd = 0.0;
                 for (int t = 0; t < d; ++t) {
                     dot += qi[t] * Kb[(size_t)j * d + t];
                     dd += doi[t] * Vb[(size_t)j * d + t];
                 }
-                s[j] = scale * dot;
-                dp[j] = dd;
+                s[j - lo] = scale * dot;
+                dp[j - lo] = dd;
             }
             double m = -INFINITY;
-            for (int j = 0; j < nvis; ++j)
-                if (s[j] > m) m = s[j];
+            for (int j = lo; j < hi; ++j)
+                if (s[j - lo] > m) m = s[j - lo];
             double l = 0.0;
-            for (int j = 0; j < nvis; ++j)
-                l += exp(s[j] - m);
+            for (int j = lo; j < hi; ++j)
+                l += exp(s[j - lo] - m);
             double Di = 0.0;
-            for (int j = 0; j < nvis; ++j)
-                Di += exp(s[j] - m) / l * dp[j];
-            lse[it] = m + log(l);
+            for (int j = lo; j < hi; ++j)
+                Di += exp(s[j - lo] - m) / l * dp[j - lo];
+            lse[it] = hi > lo ? m + log(l) : -INFINITY;
             Drow[it] = Di;
             const int r = want[it];
             if (r >= 0) {
                 double *dqi = dq + ((size_t)bh * nr + r) * d;
                 for (int t = 0; t < d; ++t)
                     dqi[t] = 0.0;
-                for (int j = 0; j < nvis; ++j) {
-                    const double p = exp(s[j] - m) / l;
-                    const double ds = p * (dp[j] - Di);
+                for (int j = lo; j < hi; ++j) {
+                    const double p = exp(s[j - lo] - m) / l;
+                    const double ds = p * (dp[j - lo] - Di);
                     for (int t = 0; t < d; ++t)
                         dqi[t] += scale * ds * Kb[(size_t)j * d + t];
                 }
@@ -157,8 +180,9 @@ int oracle_attention_bwd_f64(const double *q, const double *k, const double *v, 
                 dkj[t] = 0.0;
                 dvj[t] = 0.0;
             }
-            const int i0 = causal ? j : 0; /* rows i >= j see key j under the mask */
-            for (int i = i0; i < Lq; ++i) {
+            int ilo, ihi;
+            rows_of_key(j, Lq, wl, wr, &ilo, &ihi);
+            for (int i = ilo; i < ihi; ++i) {
                 const double *qi = q + ((size_t)bh * Lq + i) * d;
                 const double *doi = dout + ((size_t)bh * Lq + i) * d;
                 double dot = 0.0, dd = 0.0;
@@ -181,4 +205,14 @@ int oracle_attention_bwd_f64(const double *q, const double *k, const double *v, 
     free(Drow);
     free(want);
     return bad ? ORACLE_ERR_NOMEM : ORACLE_OK;
+}
+
+int oracle_attention_bwd_f64(const double *q, const double *k, const double *v, const double *dout,
+                             int B, int H, int Lq, int Lk, int d, double scale, int causal,
+                             const int64_t *rows, int nrows, const int64_t *keys, int nkeys,
+                             double *dq, double *dk, double *dv, int nthreads)
+{
+    if (causal != 0 && causal != 1) return ORACLE_ERR_ARG;
+    return oracle_attention_bwd_window_f64(q, k, v, dout, B, H, Lq, Lk, d, scale, -1, causal ? 0 : -1,
+                                           rows, nrows, keys, nkeys, dq, dk, dv, nthreads);
 }

@@ -62,6 +62,14 @@ def _lib():
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.oracle_attention_bwd_window_f64.restype = ctypes.c_int
+        lib.oracle_attention_bwd_window_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         _LIB = lib
     return _LIB
 
@@ -159,7 +167,7 @@ def _index_rows(idx, BH):
     return np.ascontiguousarray(a.reshape(BH, -1), dtype=np.int64)
 
 
-def attention_bwd_f64(q, k, v, dout, scale, causal, rows=None, keys=None, nthreads=None):
+def attention_bwd_f64(q, k, v, dout, scale, causal, rows=None, keys=None, nthreads=None, window=None):
     """Gradients of exact attention in float64: (dq, dk, dv) for the upstream gradient dout.
 
     The chain rule through the definition computed by ``attention_f64``:
@@ -171,7 +179,9 @@ def attention_bwd_f64(q, k, v, dout, scale, causal, rows=None, keys=None, nthrea
 
     q, dout: [B, H, Lq, d]; k, v: [B, H, Lk, d].  rows / keys: None for all, else
     index arrays [B*H, n] (or [n] shared by every head) selecting the query rows
-    of dq and the keys of dk, dv.  Returns dq [B, H, nr, d], dk, dv [B, H, nk, d].
+    of dq and the keys of dk, dv.  window: None, or (window_left, window_right) of
+    ``attention_window_f64`` (causal is then ignored); rows that see no key get
+    dq = 0 and contribute nothing.  Returns dq [B, H, nr, d], dk, dv [B, H, nk, d].
     """
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -189,9 +199,13 @@ def attention_bwd_f64(q, k, v, dout, scale, causal, rows=None, keys=None, nthrea
     dv = np.empty((B, H, nk, d))
     if nthreads is None:
         nthreads = default_threads()
-    rc = _lib().oracle_attention_bwd_f64(
+    if window is None:
+        fn, mask = _lib().oracle_attention_bwd_f64, (int(bool(causal)),)
+    else:
+        fn, mask = _lib().oracle_attention_bwd_window_f64, (int(window[0]), int(window[1]))
+    rc = fn(
         q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
-        B, H, Lq, Lk, d, float(scale), int(bool(causal)),
+        B, H, Lq, Lk, d, float(scale), *mask,
         rows_arr.ctypes.data if rows_arr is not None else None, nr,
         keys_arr.ctypes.data if keys_arr is not None else None, nk,
         dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(nthreads))

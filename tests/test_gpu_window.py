@@ -78,3 +78,48 @@ def test_window_matches_plain_forward(causal):
     torch.cuda.synchronize()
     assert torch.max(torch.abs(o1.float() - o2.float())).item() <= 1e-2
     assert torch.max(torch.abs(l1 - l2)).item() <= 1e-5
+
+
+# ------------------------------------------------------------------ backward
+BWD_CASES = [
+    # B, H, Lq, Lk, d, wl, wr
+    (1, 2, 300, 300, 64, 16, 0),
+    (1, 1, 500, 500, 128, 100, 0),
+    (2, 1, 257, 255, 128, 31, 7),
+    (1, 1, 200, 600, 64, 64, 64),
+    (1, 1, 400, 100, 64, 10, 0),        # rows >= 111 see no key; keys seen by few rows
+    (1, 1, 333, 333, 128, 0, 0),
+    (1, 2, 384, 512, 128, -1, 50),
+    (1, 1, 640, 640, 64, 127, -1),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_window_backward_parity(case):
+    from flashattention_forward_fwd_amd.inputs import random_dout
+    from tests.test_gpu_bwd import compare_grads
+    B, H, Lq, Lk, d, wl, wr = case
+    seed = sum(case) + 5
+    q, k, v = random_qkv(B, H, Lq, Lk, d, "bf16", seed=seed)
+    do = random_dout(B, H, Lq, d, "bf16", seed=seed)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    say("case window bwd %s" % (case,))
+    tq, tk, tv, tdo = (t.cuda() for t in (q, k, v, do))
+    o, lse = fa.forward(tq, tk, tv, scale=scale, window=(wl, wr))
+    grads = fa.backward(tq, tk, tv, o, lse, tdo, scale=scale, window=(wl, wr))
+    torch.cuda.synchronize()
+    got = tuple(g.double().cpu().numpy() for g in grads)
+    want = ref.attention_bwd_f64(widen(q), widen(k), widen(v), widen(do), scale, False, window=(wl, wr))
+    compare_grads("window bwd %s" % (case,), got, want)
+
+
+def test_window_backward_causal_matches_fa2_bwd():
+    """(-1, 0) through fa2_bwd_window gives fa2_bwd's causal gradients bit for bit."""
+    from flashattention_forward_fwd_amd.inputs import random_dout
+    q, k, v = (t.cuda() for t in random_qkv(1, 2, 700, 700, 128, "bf16", seed=50))
+    do = random_dout(1, 2, 700, 128, "bf16", seed=50).cuda()
+    o, lse = fa.forward(q, k, v, causal=True)
+    g1 = fa.backward(q, k, v, o, lse, do, causal=True)
+    g2 = fa.backward(q, k, v, o, lse, do, window=(-1, 0))
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))

@@ -140,7 +140,61 @@ def pin_sampled(bwd):
             np.testing.assert_allclose(dvs[b, h], dv[b, h, keys[bh]], atol=0)
 
 
-PINS = [pin_torch_autograd, pin_finite_differences, pin_closed_forms, pin_identities, pin_sampled]
+def pin_window_autograd(bwd):
+    """Windows: PyTorch float64 autograd through its attention with a boolean mask
+    (rows without a visible key left out of the loss, where torch gives NaN), the
+    full / causal cases, and central differences of the window forward oracle."""
+    rng = np.random.default_rng(36)
+    for (Lq, Lk, d, wl, wr) in [(13, 13, 8, 3, 0), (11, 17, 4, 2, 5), (16, 9, 8, 4, 1), (9, 9, 4, -1, 2),
+                                (10, 10, 4, 0, -1), (12, 5, 4, 1, 0)]:
+        q, k, v = _rand((1, 2, Lq, d), rng), _rand((1, 2, Lk, d), rng), _rand((1, 2, Lk, d), rng)
+        dout = _rand((1, 2, Lq, d), rng)
+        i = np.arange(Lq)[:, None]
+        j = np.arange(Lk)[None, :]
+        m = np.ones((Lq, Lk), dtype=bool)
+        if wl >= 0:
+            m &= j >= i - wl
+        if wr >= 0:
+            m &= j <= i + wr
+        live = m.any(axis=1)
+        do_live = dout * live[None, None, :, None]           # empty rows carry no gradient
+        got = bwd(q, k, v, do_live, 0.5, False, window=(wl, wr))
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(m), scale=0.5)
+        (o[:, :, torch.from_numpy(live)] * torch.from_numpy(dout)[:, :, torch.from_numpy(live)]).sum().backward()
+        for g, w in zip(got, (tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy())):
+            np.testing.assert_allclose(g, w, rtol=0, atol=1e-12)
+        # with every row live, empty-row handling aside, the gradients do not depend on dO of empty rows
+        got2 = bwd(q, k, v, dout, 0.5, False, window=(wl, wr))
+        for g, w in zip(got2, got):
+            np.testing.assert_allclose(g, w, rtol=0, atol=1e-12)
+    q, k, v = _rand((1, 1, 9, 4), rng), _rand((1, 1, 9, 4), rng), _rand((1, 1, 9, 4), rng)
+    dout = _rand((1, 1, 9, 4), rng)
+    for causal, win in ((False, (-1, -1)), (True, (-1, 0)), (True, (20, 0))):
+        for g, w in zip(bwd(q, k, v, dout, 0.4, False, window=win), bwd(q, k, v, dout, 0.4, causal)):
+            np.testing.assert_allclose(g, w, rtol=0, atol=1e-13)
+    # central differences of the window forward oracle
+    h = 1e-5
+    q, k, v = _rand((1, 1, 6, 3), rng), _rand((1, 1, 7, 3), rng), _rand((1, 1, 7, 3), rng)
+    dout = _rand((1, 1, 6, 3), rng)
+    dq, dk, dv = bwd(q, k, v, dout, 0.6, False, window=(2, 1))
+
+    def loss(qq, kk, vv):
+        o, _ = ref.attention_window_f64(qq, kk, vv, 0.6, 2, 1, nthreads=1)
+        return float((o * dout).sum())
+
+    for which, x, g in ((0, q, dq), (1, k, dk), (2, v, dv)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            a, b = [q.copy(), k.copy(), v.copy()], [q.copy(), k.copy(), v.copy()]
+            a[which][idx] += h
+            b[which][idx] -= h
+            fd[idx] = (loss(*a) - loss(*b)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=0, atol=1e-8)
+
+
+PINS = [pin_torch_autograd, pin_finite_differences, pin_closed_forms, pin_identities, pin_sampled,
+        pin_window_autograd]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -158,15 +212,19 @@ def test_bwd_oracle_rejects_bad_arguments():
 
 # ----------------------------------------------------- planted mistakes (CPU only)
 MUTANTS = {
-    "row_term_sign": ("const double ds = p * (dp[j] - Di);", "const double ds = p * (dp[j] + Di);"),
+    "row_term_sign": ("const double ds = p * (dp[j - lo] - Di);", "const double ds = p * (dp[j - lo] + Di);"),
     "row_term_dropped_in_dk": ("const double ds = p * (dd - Drow[bh * Lq + i]);", "const double ds = p * dd;"),
     "dk_scale_dropped": ("dkj[t] += scale * ds * qi[t];", "dkj[t] += ds * qi[t];"),
     "dv_weighted_by_ds": ("dvj[t] += p * doi[t];", "dvj[t] += ds * doi[t];"),
-    "causal_key_start": ("const int i0 = causal ? j : 0;", "const int i0 = causal ? j + 1 : 0;"),
+    "key_rows_start_late": ("if (wr >= 0 && (int64_t)j - wr > a) a = (int64_t)j - wr;",
+                            "if (wr >= 0 && (int64_t)j - wr + 1 > a) a = (int64_t)j - wr + 1;"),
     "dq_reads_v": ("dqi[t] += scale * ds * Kb[(size_t)j * d + t];", "dqi[t] += scale * ds * Vb[(size_t)j * d + t];"),
-    "lse_without_sum": ("lse[it] = m + log(l);", "lse[it] = m;"),
+    "lse_without_sum": ("lse[it] = hi > lo ? m + log(l) : -INFINITY;", "lse[it] = hi > lo ? m : -INFINITY;"),
     "dp_from_k": ("dd += doi[t] * Vb[(size_t)j * d + t];", "dd += doi[t] * Kb[(size_t)j * d + t];"),
-    "causal_ignored_in_rows": ("if (causal && i + 1 < Lk) nvis = i + 1;", "if (0 && i + 1 < Lk) nvis = i + 1;"),
+    "causal_ignored_in_rows": ("if (wr >= 0 && (int64_t)i + wr + 1 < b) b = (int64_t)i + wr + 1;",
+                               "if (0 && (int64_t)i + wr + 1 < b) b = (int64_t)i + wr + 1;"),
+    "window_left_ignored_for_keys": ("if (wl >= 0 && (int64_t)j + wl + 1 < b) b = (int64_t)j + wl + 1;",
+                                     "if (0 && (int64_t)j + wl + 1 < b) b = (int64_t)j + wl + 1;"),
 }
 
 
@@ -182,17 +240,23 @@ def _load_mutant(name, tmp_path):
     fn = lib.oracle_attention_bwd_f64
     fn.restype = ctypes.c_int
     fn.argtypes = ref._lib().oracle_attention_bwd_f64.argtypes
+    fnw = lib.oracle_attention_bwd_window_f64
+    fnw.restype = ctypes.c_int
+    fnw.argtypes = ref._lib().oracle_attention_bwd_window_f64.argtypes
 
     class _Shim:
         """The real library for the forward, the mutant for the backward."""
         oracle_attention_f64 = ref._lib().oracle_attention_f64
+        oracle_attention_window_f64 = ref._lib().oracle_attention_window_f64
         oracle_attention_bwd_f64 = fn
+        oracle_attention_bwd_window_f64 = fnw
 
-    def bwd(q, k, v, dout, scale, causal, rows=None, keys=None):
+    def bwd(q, k, v, dout, scale, causal, rows=None, keys=None, window=None):
         saved = ref._LIB
         ref._LIB = _Shim
         try:
-            return ref.attention_bwd_f64(q, k, v, dout, scale, causal, rows=rows, keys=keys, nthreads=1)
+            return ref.attention_bwd_f64(q, k, v, dout, scale, causal, rows=rows, keys=keys, nthreads=1,
+                                         window=window)
         finally:
             ref._LIB = saved
     return bwd
@@ -202,7 +266,7 @@ def _load_mutant(name, tmp_path):
 def test_planted_mistakes_are_caught(name, tmp_path):
     bwd = _load_mutant(name, tmp_path)
     caught = []
-    for pin in (pin_torch_autograd, pin_closed_forms, pin_identities):
+    for pin in (pin_torch_autograd, pin_closed_forms, pin_identities, pin_window_autograd):
         try:
             with np.errstate(all="ignore"):
                 pin(bwd)
