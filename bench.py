@@ -140,6 +140,9 @@ def main():
                     help="time the sliding-window forward fa2_fwd_window (key j visible to query i iff "
                          "i-WL <= j <= i+WR; negative: unbounded) on a bf16 workload; the window "
                          "replaces the workload's causal flag")
+    ap.add_argument("--fp16", action="store_true",
+                    help="run a bf16 workload's shapes in fp16 (fa2_fwd_f16 / fa2_bwd_f16): inputs drawn the same "
+                         "way, rounded to IEEE half")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass fa2_bwd (bf16 workloads) instead of the forward")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -164,6 +167,12 @@ def main():
         sys.exit(1)
     fa.lib()   # fail loudly if the HIP library is missing
     w = dict(WORKLOADS, **DECODE_WORKLOADS)[args.workload or HEADLINE]
+    if args.fp16:
+        import dataclasses
+        if w.dtype != "bf16" or args.splits is not None or args.window is not None:
+            print("bench.py: --fp16 takes a bf16 workload, without --splits or --window", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, dtype="fp16")
     q, k, v = workload_inputs(w)
     dq, dk, dv = q.cuda(), k.cuda(), v.cuda()
     o = torch.empty_like(dq)
@@ -191,24 +200,24 @@ def main():
         win_info = {"window_left": wl, "window_right": wr, "visible_pairs_per_head": pairs,
                     "flops_count": "4*d per visible (query, key) pair"}
     elif args.backward:
-        if w.dtype != "bf16" or args.splits is not None:
-            print("bench.py: --backward takes a bf16 workload and no --splits", file=sys.stderr)
+        if w.dtype not in ("bf16", "fp16") or args.splits is not None:
+            print("bench.py: --backward takes a bf16 (or --fp16) workload and no --splits", file=sys.stderr)
             sys.exit(2)
         from flashattention_forward_fwd_amd.inputs import random_dout
-        do = random_dout(w.B, w.H, w.Lq, w.d, "bf16", seed=w.seed)
+        do = random_dout(w.B, w.H, w.Lq, w.d, w.dtype, seed=w.seed)
         ddo = do.cuda()
-        fa.fa2_fwd(*(args_common + (stream.cuda_stream,)))
+        (fa.fa2_fwd_f16 if w.dtype == "fp16" else fa.fa2_fwd)(*(args_common + (stream.cuda_stream,)))
         gq, gk, gv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
         ws_bytes = fa.fa2_bwd_workspace_bytes(w.B, w.H, w.Lq)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-        fn = fa.fa2_bwd
+        fn = fa.fa2_bwd_f16 if w.dtype == "fp16" else fa.fa2_bwd
         call = (dq, dk, dv, o, lse, ddo, gq, gk, gv, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal),
                 workspace, ws_bytes, stream.cuda_stream)
         bwd_info = {"timed_call": "fa2_bwd = prep + dK/dV + dQ kernels", "workspace_bytes": ws_bytes,
                     "flops_count": "2.5x forward (S, dP, dV, dK, dQ); the dQ pass recomputes S and dP, "
                                    "so the device executes 3.5x"}
     elif args.splits is None:
-        fn = fa.fa2_fwd if w.dtype == "bf16" else fa.fa2_fwd_f32
+        fn = {"bf16": fa.fa2_fwd, "fp16": fa.fa2_fwd_f16, "fp32": fa.fa2_fwd_f32}[w.dtype]
         call = args_common + (stream.cuda_stream,)
     else:
         if w.dtype != "bf16":
@@ -245,9 +254,11 @@ def main():
 
     flops = flops_override if flops_override is not None else w.flops * (2.5 if bwd_info else 1.0)
     value = flops / (ms_step * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
-    traffic = stored_traffic(w.name) if split_info is None and bwd_info is None and win_info is None else None
-    algo_bytes = (2 if w.dtype == "bf16" else 4) * w.B * w.H * (2 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq
+    # dense fp16 MFMA has the same published peak as bf16 on MI355X
+    peak = PEAK_FP32_MFMA_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
+    traffic = (stored_traffic(w.name) if split_info is None and bwd_info is None and win_info is None
+               and not args.fp16 else None)
+    algo_bytes = (4 if w.dtype == "fp32" else 2) * w.B * w.H * (2 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq
     if bwd_info:
         # reads q, k, v, o, dout, lse; writes dq, dk, dv
         algo_bytes = 2 * w.B * w.H * (3 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq \
@@ -276,6 +287,8 @@ def main():
     }
     if split_info is not None:
         out["config"]["split_kv"] = split_info
+    if args.fp16:
+        out["metric"] = out["metric"].replace("bf16", "fp16")
     if win_info is not None:
         out["config"]["window"] = win_info
         out["metric"] = "attention fwd TFLOPS (4·d per visible query-key pair) bf16, sliding window"

@@ -10,13 +10,15 @@ and the stream.
 """
 import math
 
-from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_window, fa2_bwd_workspace_bytes,  # noqa: F401
-                   fa2_check_args, fa2_fwd, fa2_fwd_f32, fa2_fwd_splitkv, fa2_fwd_window, fa2_merge_partials,
+from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_f16, fa2_bwd_window,  # noqa: F401
+                   fa2_bwd_workspace_bytes,
+                   fa2_check_args, fa2_fwd, fa2_fwd_f16, fa2_fwd_f32, fa2_fwd_splitkv, fa2_fwd_window,
+                   fa2_merge_partials,
                    fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib, status_string)
 
-__all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f32", "fa2_fwd_splitkv",
+__all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f16", "fa2_fwd_f32", "fa2_fwd_splitkv",
            "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
-           "fa2_fwd_window", "fa2_bwd", "fa2_bwd_window", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
+           "fa2_fwd_window", "fa2_bwd", "fa2_bwd_f16", "fa2_bwd_window", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
            "FA2_MAX_SPLITS"]
 
 
@@ -24,7 +26,7 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
             window=None):
     """O = softmax(scale * Q K^T [causal]) V and the per-row logsumexp.
 
-    q: [B, H, Lq, d], k and v: [B, H, Lk, d], all bf16 or all fp32 CUDA tensors
+    q: [B, H, Lq, d], k and v: [B, H, Lk, d], all bf16, all fp16 or all fp32 CUDA tensors
     (made contiguous).  scale defaults to fp32(1/sqrt(d)).  Returns (o, lse)
     with o like q and lse fp32 [B, H, Lq].  Enqueued on the current stream.
 
@@ -41,8 +43,8 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
 
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be device tensors (no CPU path)")
-    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16, all float16 or all float32")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, L, d]")
     B, H, Lq, d = q.shape
@@ -75,7 +77,7 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
         fa2_fwd_splitkv(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, num_splits, workspace,
                         workspace.numel() * workspace.element_size(), stream)
         return out, lse
-    fn = fa2_fwd if q.dtype == torch.bfloat16 else fa2_fwd_f32
+    fn = {torch.bfloat16: fa2_fwd, torch.float16: fa2_fwd_f16, torch.float32: fa2_fwd_f32}[q.dtype]
     fn(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, stream)
     return out, lse
 
@@ -111,7 +113,7 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
              window=None):
     """Gradients (dq, dk, dv) of attention for the upstream gradient dout (libfa2 ``fa2_bwd``).
 
-    q, k, v, o, dout: bfloat16 CUDA tensors (q, o, dout [B, H, Lq, d]; k, v
+    q, k, v, o, dout: bfloat16 (or all float16) CUDA tensors (q, o, dout [B, H, Lq, d]; k, v
     [B, H, Lk, d]), o and lse (fp32 [B, H, Lq]) as returned by ``forward`` for
     the same q, k, v, causal and scale.  Returns bf16 (dq, dk, dv).  The
     workspace is allocated here unless a large enough uint8 device tensor is
@@ -124,8 +126,9 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
     ts = (q, k, v, o, dout)
     if not all(t.is_cuda for t in ts) or not lse.is_cuda:
         raise ValueError("all tensors must be device tensors (no CPU path)")
-    if any(t.dtype != torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
-        raise ValueError("q, k, v, o, dout must be bfloat16 and lse float32")
+    if any(t.dtype != q.dtype for t in ts) or q.dtype not in (torch.bfloat16, torch.float16) \
+            or lse.dtype != torch.float32:
+        raise ValueError("q, k, v, o, dout must be all bfloat16 or all float16, and lse float32")
     if any(t.dim() != 4 for t in ts):
         raise ValueError("q, k, v, o, dout must be [B, H, L, d]")
     B, H, Lq, d = q.shape
@@ -148,10 +151,11 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
     stream = torch.cuda.current_stream(q.device).cuda_stream
     nbytes = workspace.numel() * workspace.element_size()
     if window is not None:
-        if causal:
-            raise ValueError("window replaces the causal mask; pass causal=False")
+        if causal or q.dtype != torch.bfloat16:
+            raise ValueError("window takes bfloat16 tensors and replaces the causal mask (causal=False)")
         fa2_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(window[0]), int(window[1]),
                        workspace, nbytes, stream)
         return dq, dk, dv
-    fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), workspace, nbytes, stream)
+    fn = fa2_bwd if q.dtype == torch.bfloat16 else fa2_bwd_f16
+    fn(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), workspace, nbytes, stream)
     return dq, dk, dv

@@ -26,6 +26,7 @@ _L = ctypes.c_int64
 SIGNATURES = {
     "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa2_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa2_fwd_f16": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa2_status_string": (ctypes.c_char_p, [_I]),
     "fa2_check_args": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
     "fa2_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
@@ -35,6 +36,7 @@ SIGNATURES = {
     "fa2_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa2_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
+    "fa2_bwd_f16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa2_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
 }
 
@@ -95,6 +97,15 @@ def fa2_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
         raise FA2Error(st, "fa2_fwd_f32")
 
 
+def fa2_fwd_f16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
+    """libfa2 ``fa2_fwd_f16``.  Tensors or raw device addresses; raises FA2Error."""
+    st = lib().fa2_fwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                           int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                           _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_fwd_f16")
+
+
 def fa2_check_args(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes):
     """libfa2 ``fa2_check_args``: the status the entry points would return (no HIP call)."""
     return lib().fa2_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -139,6 +150,16 @@ def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, w
                        _ptr(workspace), int(workspace_bytes), _ptr(stream))
     if st != FA2_OK:
         raise FA2Error(st, "fa2_bwd")
+
+
+def fa2_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+                workspace_bytes, stream):
+    """libfa2 ``fa2_bwd_f16`` (fp16 gradients).  Raises FA2Error."""
+    st = lib().fa2_bwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                           _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                           _ptr(workspace), int(workspace_bytes), _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_bwd_f16")
 
 
 def fa2_bwd_workspace_bytes(B, H, Lq):

@@ -220,6 +220,18 @@ int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
     return FA2_OK;
 }
 
+int fa2_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p);
+    if (st != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (fa2::launch_fwd_f16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
 int fa2_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
 {
@@ -336,6 +348,20 @@ int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const fl
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     if (fa2::launch_bwd_bf16(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fa2_bwd_f16(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                void *workspace, size_t workspace_bytes_given, void *stream)
+{
+    fa2::BwdParams p;
+    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+                         workspace_bytes_given, &p);
+    if (st != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (fa2::launch_bwd_f16(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
         return FA2_ERR_LAUNCH;
     return FA2_OK;
 }

@@ -1,4 +1,4 @@
-// fa2_bwd.hip -- FlashAttention-2 backward pass, bf16 in/out, for gfx950.
+// fa2_bwd.hip -- FlashAttention-2 backward pass, bf16 or fp16 in/out, for gfx950.
 //
 // The backward needs the probabilities P of the forward but the forward keeps
 // only O and one logsumexp per row, so every score block is rebuilt from Q, K
@@ -39,8 +39,14 @@
 namespace fa2 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// bf16 (E = __bf16) or fp16 (E = _Float16) elements: 8- and 4-element vectors
+// of E and the 32x32x16 matrix-core product for each.
+template <typename E> struct V16 {
+    typedef E x8 __attribute__((ext_vector_type(8)));
+    typedef E x4 __attribute__((ext_vector_type(4)));
+};
+typedef V16<__bf16>::x8 bf16x8;
+typedef V16<_Float16>::x8 f16x8;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
@@ -48,6 +54,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 constexpr int kRawBufferFlags = 0x00020000;   // raw buffer access, gfx9 resource word 3
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -102,10 +117,10 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t src, int row0, 
 }
 
 // A operand contracting over d: row `row` of a tile, logical d chunk 16c + 8hh.
-template <int D>
-__device__ __forceinline__ bf16x8 read_rows_op(const LDS_AS char *tile, int row, int c, int hh)
+template <int D, typename E>
+__device__ __forceinline__ typename V16<E>::x8 read_rows_op(const LDS_AS char *tile, int row, int c, int hh)
 {
-    return *reinterpret_cast<const LDS_AS bf16x8 *>(tile + BTile<D>::addr(row, 2 * (16 * c + 8 * hh)));
+    return *reinterpret_cast<const LDS_AS typename V16<E>::x8 *>(tile + BTile<D>::addr(row, 2 * (16 * c + 8 * hh)));
 }
 
 // Transposed A operand for a product contracting over the tile's rows: lane l
@@ -113,44 +128,46 @@ __device__ __forceinline__ bf16x8 read_rows_op(const LDS_AS char *tile, int row,
 // 16c + 8 + 4hh + 0..3 (slots 4-7), hh = l / 32.  Lane 16g + 4e + r supplies the
 // address of row 4(g/2) + e (+16c, +8 for the second read), columns
 // 32 dt + 16(g%2) + 4r .. +3.
-template <int D>
-__device__ __forceinline__ bf16x8 read_cols_op(const LDS_AS char *tile, int dt, int c, int lane)
+template <int D, typename E>
+__device__ __forceinline__ typename V16<E>::x8 read_cols_op(const LDS_AS char *tile, int dt, int c, int lane)
 {
     const int g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
     const int row = 16 * c + 4 * (g >> 1) + e;
     const int x = 2 * (32 * dt + 16 * (g & 1) + 4 * r);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(tile + BTile<D>::addr(row, x)));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(tile + BTile<D>::addr(row + 8, x)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(typename V16<E>::x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 16 bytes of a bf16 row from global memory (zero when `valid` is false).
-__device__ __forceinline__ bf16x8 load_row_chunk(const uint16_t *p, bool valid)
+// 16 bytes of a 16-bit row from global memory (zero when `valid` is false).
+template <typename E>
+__device__ __forceinline__ typename V16<E>::x8 load_row_chunk(const uint16_t *p, bool valid)
 {
     u32x4 raw = {0u, 0u, 0u, 0u};
     if (valid) raw = *reinterpret_cast<const u32x4 *>(p);
-    return __builtin_bit_cast(bf16x8, raw);
+    return __builtin_bit_cast(typename V16<E>::x8, raw);
 }
 
 // Store one lane's share of a transposed accumulator (rows = d, columns =
 // token) as bf16: the lane holds column l % 32 (token `row`), d positions
 // 32 dt + 8a + 4hh + 0..3 in accumulator entries 4a .. 4a+3.
-template <int D>
+template <int D, typename E>
 __device__ __forceinline__ void store_tokens(uint16_t *dst_row, const f32x16 (&acc)[D / 32], float mul, int hh)
 {
+    using e4 = typename V16<E>::x4;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const f32x4 v4 = {acc[dt][4 * a + 0] * mul, acc[dt][4 * a + 1] * mul, acc[dt][4 * a + 2] * mul,
                               acc[dt][4 * a + 3] * mul};
-            *reinterpret_cast<bf16x4 *>(dst_row + 32 * dt + 8 * a + 4 * hh) = __builtin_convertvector(v4, bf16x4);
+            *reinterpret_cast<e4 *>(dst_row + 32 * dt + 8 * a + 4 * hh) = __builtin_convertvector(v4, e4);
         }
 }
 
 // ---------------------------------------------------------------- 1. prep
 // D_i = sum_t dO_it O_it (fp32) and lse2_i = lse_i * log2(e); D/8 threads per row.
-template <int D>
+template <int D, typename E>
 __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, const uint16_t *dout, const float *lse,
                                                            float *lse2, float *delta, int64_t rows)
 {
@@ -160,13 +177,11 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
     const int part = (int)(gid % kTpr);
     float acc = 0.f;
     if (row < rows) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(o + row * D + 8 * part);
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(dout + row * D + 8 * part);
+        const f32x8 a = __builtin_convertvector(*reinterpret_cast<const typename V16<E>::x8 *>(o + row * D + 8 * part), f32x8);
+        const f32x8 b = __builtin_convertvector(*reinterpret_cast<const typename V16<E>::x8 *>(dout + row * D + 8 * part), f32x8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc = __builtin_fmaf(__uint_as_float(a[i] << 16), __uint_as_float(b[i] << 16), acc);
-            acc = __builtin_fmaf(__uint_as_float(a[i] & 0xffff0000u), __uint_as_float(b[i] & 0xffff0000u), acc);
-        }
+        for (int i = 0; i < 8; ++i)
+            acc = __builtin_fmaf(a[i], b[i], acc);
     }
 #pragma unroll
     for (int off = kTpr / 2; off > 0; off >>= 1)
@@ -195,11 +210,12 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * kWave;
 
-template <int D, bool MASKED>
+template <int D, bool MASKED, typename E>
 __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dkdv_kernel(BwdParams p)
 {
     using T = BTile<D>;
+    using e8 = typename V16<E>::x8;
     constexpr int kDc = D / 16;
     constexpr int kDt = D / 32;
     constexpr int kTileElems = kRowTile * D;
@@ -210,8 +226,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     __shared__ __attribute__((aligned(1024))) uint16_t sO1[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sO2[kTileElems];
     // P of one tile: [key group][chunk c][lane] x 16 bytes, in the lane order of the B operand
-    __shared__ __attribute__((aligned(1024))) bf16x8 sP0[kWaves * 4 * kWave];
-    __shared__ __attribute__((aligned(1024))) bf16x8 sP1[kWaves * 4 * kWave];
+    __shared__ __attribute__((aligned(1024))) e8 sP0[kWaves * 4 * kWave];
+    __shared__ __attribute__((aligned(1024))) e8 sP1[kWaves * 4 * kWave];
     // per buffer: lse2 of the tile's 64 rows, then their D
     __shared__ __attribute__((aligned(256))) float sStat0[128];
     __shared__ __attribute__((aligned(256))) float sStat1[128];
@@ -279,10 +295,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     // K (dV wavefronts) or V (dK wavefronts) of this lane's key as B operands
     // (d chunk 16c + 8hh); zero past Lk.
     const uint16_t *Xr = static_cast<const uint16_t *>(is_dk ? p.v : p.k) + ((size_t)bh * p.Lk + key) * D;
-    bf16x8 xf[kDc];
+    e8 xf[kDc];
 #pragma unroll
     for (int c = 0; c < kDc; ++c)
-        xf[c] = load_row_chunk(Xr + 16 * c + 8 * hh, key < p.Lk);
+        xf[c] = load_row_chunk<E>(Xr + 16 * c + 8 * hh, key < p.Lk);
 
     f32x16 acc[kDt];                       // dV^T (wavefronts 0-3) or dK^T (4-7)
 #pragma unroll
@@ -310,8 +326,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                     s[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(qb, 32 * h + l32, c, hh),
-                                                                       xf[c], s[h], 0, 0, 0);
+                        s[h] = mfma_32x32x16(read_rows_op<D, E>(qb, 32 * h + l32, c, hh), xf[c], s[h]);
                 }
                 // Does every (row, key) pair of this tile and key group lie in the window?
                 const bool need_mask =
@@ -319,8 +334,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                                 (p.wr < 0 || (int64_t)kw0 + kKeysPerWave - 1 <= (int64_t)t * kRowTile + p.wr));
                 // Chunk c (B operand of the products over the tile's rows) holds
                 // rows 16c + 8(e/4) + 4hh + e%4, e = 0..7: entries 8(c%2) + e of half c/2.
-                LDS_AS bf16x8 *pdst = (LDS_AS bf16x8 *)((t & 1) ? sP1 : sP0) + grp * 4 * kWave;
-                bf16x8 pf[4];
+                LDS_AS e8 *pdst = (LDS_AS e8 *)((t & 1) ? sP1 : sP0) + grp * 4 * kWave;
+                e8 pf[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int h = c >> 1, i0 = 8 * (c & 1);
@@ -338,7 +353,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                         }
                         v8[e] = pv;
                     }
-                    pf[c] = __builtin_convertvector(v8, bf16x8);
+                    pf[c] = __builtin_convertvector(v8, e8);
                     pdst[c * kWave + lane] = pf[c];
                 }
                 // dV^T += dO^T P (contraction over the tile's rows).
@@ -346,8 +361,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(ob, dt, c, lane), pf[c],
-                                                                          acc[dt], 0, 0, 0);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, dt, c, lane), pf[c], acc[dt]);
             }
         } else {
             const int tk = t - 1;
@@ -363,30 +377,28 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                     dp[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(ob, 32 * h + l32, c, hh),
-                                                                        xf[c], dp[h], 0, 0, 0);
+                        dp[h] = mfma_32x32x16(read_rows_op<D, E>(ob, 32 * h + l32, c, hh), xf[c], dp[h]);
                 }
-                const LDS_AS bf16x8 *psrc = (const LDS_AS bf16x8 *)((tk & 1) ? sP1 : sP0) + grp * 4 * kWave;
-                bf16x8 dsf[4];
+                const LDS_AS e8 *psrc = (const LDS_AS e8 *)((tk & 1) ? sP1 : sP0) + grp * 4 * kWave;
+                e8 dsf[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int h = c >> 1, i0 = 8 * (c & 1);
-                    const bf16x8 pc = psrc[c * kWave + lane];
+                    const e8 pc = psrc[c * kWave + lane];
                     const f32x4 d4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 4 * hh);
                     const f32x4 d4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 8 + 4 * hh);
                     f32x8 v8;
 #pragma unroll
                     for (int e = 0; e < 8; ++e)   // dS = P (dP - D)
                         v8[e] = (float)pc[e] * (dp[h][i0 + e] - (e < 4 ? d4a[e] : d4b[e - 4]));
-                    dsf[c] = __builtin_convertvector(v8, bf16x8);
+                    dsf[c] = __builtin_convertvector(v8, e8);
                 }
                 // dK^T += Q^T dS (contraction over the tile's rows).
 #pragma unroll
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(qb, dt, c, lane), dsf[c],
-                                                                          acc[dt], 0, 0, 0);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, dt, c, lane), dsf[c], acc[dt]);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads of tile t+1 have landed
@@ -395,16 +407,17 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 
     if (key >= p.Lk) return;
     const size_t kv_row = (size_t)bh * p.Lk + key;
-    if (is_dk) store_tokens<D>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc, p.scale, hh);
-    else       store_tokens<D>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc, 1.0f, hh);
+    if (is_dk) store_tokens<D, E>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc, p.scale, hh);
+    else       store_tokens<D, E>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc, 1.0f, hh);
 }
 
 // ---------------------------------------------------------------- 3. dQ
-template <int D, bool MASKED>
+template <int D, bool MASKED, typename E>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_bwd_dq_kernel(BwdParams p)
 {
     using T = BTile<D>;
+    using e8 = typename V16<E>::x8;
     constexpr int kDc = D / 16;
     constexpr int kDt = D / 32;
     constexpr int kTileElems = kBc * D;
@@ -471,11 +484,11 @@ void fa2_bwd_dq_kernel(BwdParams p)
     const size_t qoff = ((size_t)bh * p.Lq + qrow);
     const uint16_t *Qr = static_cast<const uint16_t *>(p.q) + qoff * D;
     const uint16_t *Or = static_cast<const uint16_t *>(p.dout) + qoff * D;
-    bf16x8 qf[kDc], of[kDc];
+    e8 qf[kDc], of[kDc];
 #pragma unroll
     for (int c = 0; c < kDc; ++c) {
-        qf[c] = load_row_chunk(Qr + 16 * c + 8 * hh, row_ok);
-        of[c] = load_row_chunk(Or + 16 * c + 8 * hh, row_ok);
+        qf[c] = load_row_chunk<E>(Qr + 16 * c + 8 * hh, row_ok);
+        of[c] = load_row_chunk<E>(Or + 16 * c + 8 * hh, row_ok);
     }
     const float lse2 = row_ok ? p.lse2[qoff] : 0.f;
     const float dlt = row_ok ? p.delta[qoff] : 0.f;
@@ -506,16 +519,14 @@ void fa2_bwd_dq_kernel(BwdParams p)
                 dp[t] = f32x16{};
 #pragma unroll
                 for (int c = 0; c < kDc; ++c)
-                    s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(kbuf, 32 * t + l32, c, hh), qf[c],
-                                                                   s[t], 0, 0, 0);
+                    s[t] = mfma_32x32x16(read_rows_op<D, E>(kbuf, 32 * t + l32, c, hh), qf[c], s[t]);
 #pragma unroll
                 for (int c = 0; c < kDc; ++c)
-                    dp[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows_op<D>(vbuf, 32 * t + l32, c, hh), of[c],
-                                                                    dp[t], 0, 0, 0);
+                    dp[t] = mfma_32x32x16(read_rows_op<D, E>(vbuf, 32 * t + l32, c, hh), of[c], dp[t]);
             }
             // Entry i of tile t is key 64(t0 + j) + 32t + 8(i/4) + 4hh + i%4.
             const bool need_mask = j < plain_lo || j >= n_plain;
-            bf16x8 dsf[4];
+            e8 dsf[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int t = c >> 1, i0 = 8 * (c & 1);
@@ -532,42 +543,41 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     }
                     ds8[e] = pv * (dp[t][i] - dlt);
                 }
-                dsf[c] = __builtin_convertvector(ds8, bf16x8);
+                dsf[c] = __builtin_convertvector(ds8, e8);
             }
             // dQ^T += K^T dS^T (contraction over the tile's keys).
 #pragma unroll
             for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols_op<D>(kbuf, dt, c, lane), dsf[c],
-                                                                      acc[dt], 0, 0, 0);
+                    acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, dt, c, lane), dsf[c], acc[dt]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     if (!row_ok) return;
-    store_tokens<D>(static_cast<uint16_t *>(p.dq) + qoff * D, acc, p.scale, hh);
+    store_tokens<D, E>(static_cast<uint16_t *>(p.dq) + qoff * D, acc, p.scale, hh);
 }
 
-template <int D>
+template <int D, typename E>
 hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const void *o, const float *lse,
                         hipStream_t stream)
 {
     const int64_t threads = rows * (D / 8);
-    hipLaunchKernelGGL((fa2_bwd_prep_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((fa2_bwd_prep_kernel<D, E>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(p.dout), lse,
                        const_cast<float *>(p.lse2), const_cast<float *>(p.delta), rows);
     BwdParams pk = p;
     pk.n_blocks = (p.Lk + kKeyBlock - 1) / kKeyBlock;
     pk.n_wg = pk.n_blocks * p.B * p.H;
-    if (masked) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
-    else        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+    if (masked) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true, E>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+    else        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false, E>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
     BwdParams pq = p;
     pq.n_blocks = (p.Lq + kBr - 1) / kBr;
     pq.n_wg = pq.n_blocks * p.B * p.H;
-    if (masked) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
-    else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    if (masked) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true, E>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false, E>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
     return hipGetLastError();
 }
 
@@ -577,8 +587,16 @@ hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
-    return d == 64 ? launch_bwd_d<64>(p, masked, rows, o, lse, stream)
-                   : launch_bwd_d<128>(p, masked, rows, o, lse, stream);
+    return d == 64 ? launch_bwd_d<64, __bf16>(p, masked, rows, o, lse, stream)
+                   : launch_bwd_d<128, __bf16>(p, masked, rows, o, lse, stream);
+}
+
+hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)p.B * p.H * p.Lq;
+    const bool masked = p.wl >= 0 || p.wr >= 0;
+    return d == 64 ? launch_bwd_d<64, _Float16>(p, masked, rows, o, lse, stream)
+                   : launch_bwd_d<128, _Float16>(p, masked, rows, o, lse, stream);
 }
 
 }  // namespace fa2

@@ -42,13 +42,28 @@
 namespace fa2 {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// The kernels run on bf16 (E = __bf16) or fp16 (E = _Float16) inputs: 8- and
+// 4-element vectors of E, and the 32x32x16 matrix-core product for each.
+template <typename E> struct V16 {
+    typedef E x8 __attribute__((ext_vector_type(8)));
+    typedef E x4 __attribute__((ext_vector_type(4)));
+};
+typedef V16<__bf16>::x8 bf16x8;
+typedef V16<_Float16>::x8 f16x8;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -132,10 +147,11 @@ __device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t src, int 
 constexpr float kRescaleThreshold = 8.0f;
 
 // S^T = K_j Q_i^T for one wavefront: two 32x32 tiles of (keys x queries).
-template <int D>
-__device__ __forceinline__ void scores(const LDS_AS char *kb, const bf16x8 (&qf)[D / 16],
+template <int D, typename E>
+__device__ __forceinline__ void scores(const LDS_AS char *kb, const typename V16<E>::x8 (&qf)[D / 16],
                                        f32x16 (&s)[2], int k_lane)
 {
+    using e8 = typename V16<E>::x8;
     using T = Tile<D>;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -143,8 +159,8 @@ __device__ __forceinline__ void scores(const LDS_AS char *kb, const bf16x8 (&qf)
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
             const int off = (32 * t * T::kRowBytes + k_lane) ^ (32 * c);
-            const bf16x8 a = *reinterpret_cast<const LDS_AS bf16x8 *>(kb + off);
-            s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], s[t], 0, 0, 0);
+            const e8 a = *reinterpret_cast<const LDS_AS e8 *>(kb + off);
+            s[t] = mfma_32x32x16(a, qf[c], s[t]);
         }
     }
 }
@@ -206,7 +222,8 @@ __device__ __forceinline__ float reference_max(float m)
 
 // P~ = 2^(S c - m) as bf16 B operands (one per 16-key chunk: slots 0-3 are keys
 // 16c + 4hh + 0..3, slots 4-7 keys 16c + 8 + 4hh + 0..3), and its row sum.
-__device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, float m, bf16x8 (&pf)[4])
+template <typename E>
+__device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, float m, typename V16<E>::x8 (&pf)[4])
 {
     float rs = 0.f;
 #pragma unroll
@@ -218,17 +235,18 @@ __device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, f
             v8[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i0 + e], c2, -m));
             rs += v8[e];
         }
-        pf[c] = __builtin_convertvector(v8, bf16x8);
+        pf[c] = __builtin_convertvector(v8, typename V16<E>::x8);
     }
     return rs;
 }
 
 // O~^T += V_j^T P~^T; the A operand of chunk c is two transposing reads
 // (keys 16c + 4hh + 0..3 and 16c + 8 + 4hh + 0..3).
-template <int D>
-__device__ __forceinline__ void accumulate_pv(const LDS_AS char *vb, const bf16x8 (&pf)[4],
+template <int D, typename E>
+__device__ __forceinline__ void accumulate_pv(const LDS_AS char *vb, const typename V16<E>::x8 (&pf)[4],
                                               f32x16 (&acc_o)[D / 32], int v_lane)
 {
+    using e8 = typename V16<E>::x8;
     using T = Tile<D>;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -238,8 +256,8 @@ __device__ __forceinline__ void accumulate_pv(const LDS_AS char *vb, const bf16x
             const int off1 = off0 + 8 * T::kRowBytes;
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off0));
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(vb + off1));
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[c], acc_o[dt], 0, 0, 0);
+            const e8 a = __builtin_bit_cast(e8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            acc_o[dt] = mfma_32x32x16(a, pf[c], acc_o[dt]);
         }
 }
 
@@ -255,19 +273,19 @@ __device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, f
 // One step of the pipelined loop for tile j: probabilities of tile j (VALU)
 // while the scores of tile j+1 run (MFMA), then O~ += P~_j V_j (MFMA) while the
 // max of tile j+1 is taken (VALU).
-template <int D, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW>
+template <int D, typename E, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW>
 __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const LDS_AS char *v_cur,
-                                               const bf16x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
+                                               const typename V16<E>::x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
                                                f32x16 (&s_cur)[2], float &m, float &lpart, float &alpha,
                                                float c2, int j, int t0, int plain_lo, int n_plain, int Lk,
                                                int qrow, int hh, int k_lane, int v_lane, int wl, int wr)
 {
     if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
-    bf16x8 pf[4];
-    const float rs = probabilities(s_cur, c2, reference_max<EMPTY_ROWS>(m), pf);
+    typename V16<E>::x8 pf[4];
+    const float rs = probabilities<E>(s_cur, c2, reference_max<EMPTY_ROWS>(m), pf);
     f32x16 s_next[2];
-    scores<D>(k_next, qf, s_next, k_lane);
-    accumulate_pv<D>(v_cur, pf, acc_o, v_lane);
+    scores<D, E>(k_next, qf, s_next, k_lane);
+    accumulate_pv<D, E>(v_cur, pf, acc_o, v_lane);
     float mt = row_max_scaled(s_next, c2);
     // The row sum and the next max are consumed after the branch below; this
     // use keeps their VALU work in this block, between the MFMAs, instead of
@@ -293,11 +311,13 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
 // (p.wl < 0 or j >= i - p.wl) and (p.wr < 0 or j <= i + p.wr); the work-group
 // visits only the tiles that hold a key visible to one of its rows, and a row
 // that sees no key gets O = 0 and LSE = -inf.
-template <int D, bool CAUSAL, bool SPLIT, bool WINDOW = false>
+template <int D, bool CAUSAL, bool SPLIT, bool WINDOW = false, typename E = __bf16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
 {
     using T = Tile<D>;
+    using e8 = typename V16<E>::x8;
+    using e4 = typename V16<E>::x4;
     static_assert(!WINDOW || (!CAUSAL && !SPLIT), "the window replaces the causal mask; no split");
     // Rows without a visible key in a visited tile range: a causal range that
     // starts after tile 0, or a window (rows at a window edge of the block).
@@ -401,13 +421,13 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         load_tile_async<D, false>(rK, t0 + 1, sK1, wave, loff);
 
     // Q fragment: lane holds Q[qrow][16c + 8hh .. +7] for every chunk c.
-    bf16x8 qf[kDc];
+    e8 qf[kDc];
 #pragma unroll
     for (int c = 0; c < kDc; ++c) {
         u32x4 raw = {0u, 0u, 0u, 0u};
         if (qrow < p.Lq)
             raw = *reinterpret_cast<const u32x4 *>(Q + (size_t)qrow * D + 16 * c + 8 * hh);
-        qf[c] = __builtin_bit_cast(bf16x8, raw);
+        qf[c] = __builtin_bit_cast(e8, raw);
     }
 
     // Per-lane LDS byte offsets.
@@ -435,7 +455,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     // Scores of the first tile.  Its max becomes the reference (O~ and l are 0).
     f32x16 s_cur[2];
     if (n_wave > 0) {
-        scores<D>((const LDS_AS char *)sK0, qf, s_cur, k_lane);
+        scores<D, E>((const LDS_AS char *)sK0, qf, s_cur, k_lane);
         if (n_plain == 0 || (WINDOW && plain_lo > 0))
             mask_scores<CAUSAL, WINDOW>(s_cur, t0 * kBc, p.Lk, qrow, hh, p.wl, p.wr);
         m = row_max_scaled(s_cur, c2);
@@ -449,7 +469,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         // even tile j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK0, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
-        pipelined_step<D, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf,
+        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf,
                                                       acc_o, s_cur, m, lpart, alpha, c2, j, t0, plain_lo, n_plain,
                                                       p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
@@ -458,7 +478,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         // odd tile j: K_{j+1} in sK0, V_j in sV1; loads K_{j+2} -> sK1, V_{j+1} -> sV0
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK1, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
-        pipelined_step<D, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf,
+        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf,
                                                       acc_o, s_cur, m, lpart, alpha, c2, j, t0, plain_lo, n_plain,
                                                       p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr);
         __builtin_amdgcn_s_waitcnt(0);
@@ -470,9 +490,9 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, odd ? sK1 : sK0, wave, loff);
         if (j + 1 < n_kv) load_tile_async<D, true>(rV, t0 + j + 1, odd ? sV0 : sV1, wave, loff);
         if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
-        bf16x8 pf[4];
-        lpart += probabilities(s_cur, c2, reference_max<kEmptyRows>(m), pf);
-        accumulate_pv<D>((const LDS_AS char *)(odd ? sV1 : sV0), pf, acc_o, v_lane);
+        e8 pf[4];
+        lpart += probabilities<E>(s_cur, c2, reference_max<kEmptyRows>(m), pf);
+        accumulate_pv<D, E>((const LDS_AS char *)(odd ? sV1 : sV0), pf, acc_o, v_lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         ++j;
@@ -516,8 +536,8 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         for (int a = 0; a < 4; ++a) {
             const f32x4 v4 = {acc_o[dt][4 * a + 0] * inv_l, acc_o[dt][4 * a + 1] * inv_l,
                               acc_o[dt][4 * a + 2] * inv_l, acc_o[dt][4 * a + 3] * inv_l};
-            const bf16x4 b4 = __builtin_convertvector(v4, bf16x4);
-            *reinterpret_cast<bf16x4 *>(O + 32 * dt + 8 * a + 4 * hh) = b4;
+            const e4 b4 = __builtin_convertvector(v4, e4);
+            *reinterpret_cast<e4 *>(O + 32 * dt + 8 * a + 4 * hh) = b4;
         }
     if (hh == 0)
         p.lse[(size_t)bh * p.Lq + qrow] = (m + __builtin_amdgcn_logf(l)) * kLn2;
@@ -547,6 +567,19 @@ hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t s
 hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
     return launch<true>(p, d, causal, stream);
+}
+
+hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t stream)
+{
+    const dim3 grid(p.n_wg), block(kThreads);
+    if (d == 64) {
+        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, true, false, false, _Float16>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, false, false, false, _Float16>), grid, block, 0, stream, p);
+    } else {
+        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, true, false, false, _Float16>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, false, false, false, _Float16>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)

@@ -112,6 +112,7 @@ __device__ __forceinline__ float halves_sum(float x)
 namespace fa2 {
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t stream);
 // Split-KV partials: p.o is the fp32 partial-output array, p.lse the partial
 // logsumexps, both indexed by (split, b*h, row).
 hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream);
@@ -120,6 +121,7 @@ hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
 // Backward: D and lse2 into p.delta / p.lse2 from o and lse, then dK/dV, then dQ,
 // for the keys p.wl / p.wr leave visible.
 hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
+hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                         int d, void *o, float *lse, hipStream_t stream);
 }  // namespace fa2

@@ -7,8 +7,8 @@ contains none of the attention arithmetic.  Both sides of every parity check
 Recipe (the same everywhere):
   * fp32 iid N(0, 1) from ``numpy.random.default_rng(seed).standard_normal``,
     drawn in the order Q, K, V from one generator;
-  * for bf16 workloads each tensor is rounded to bfloat16 with round-to-nearest-even
-    (PyTorch's CPU conversion); a Q multiplier (the ragged workload uses 4, a power
+  * for bf16 (fp16) workloads each tensor is rounded to bfloat16 (IEEE half) with
+    round-to-nearest-even (PyTorch's CPU conversion); a Q multiplier (the ragged workload uses 4, a power
     of two) is applied after rounding, so it is exact;
   * scale = fp32(1 / sqrt(d));  layout [B, H, L, d] contiguous.
 """
@@ -26,7 +26,7 @@ class Workload:
     Lq: int
     Lk: int
     d: int
-    dtype: str          # "fp32" or "bf16"
+    dtype: str          # "fp32" or "bf16" ("fp16" for the half-precision variants)
     causal: bool
     seed: int
     q_mult: float = 1.0
@@ -70,7 +70,7 @@ def random_qkv(B, H, Lq, Lk, d, dtype="bf16", seed=0, q_mult=1.0):
     q = rng.standard_normal((B, H, Lq, d), dtype=np.float32)
     k = rng.standard_normal((B, H, Lk, d), dtype=np.float32)
     v = rng.standard_normal((B, H, Lk, d), dtype=np.float32)
-    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
     tq, tk, tv = (torch.from_numpy(a).to(tdt) for a in (q, k, v))
     if q_mult != 1.0:
         tq = tq * q_mult
@@ -83,7 +83,7 @@ def random_dout(B, H, Lq, d, dtype="bf16", seed=0):
     rounded to the requested dtype like Q, K, V."""
     rng = np.random.default_rng([seed, 4])
     a = rng.standard_normal((B, H, Lq, d), dtype=np.float32)
-    tdt = {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[dtype]
     return torch.from_numpy(a).to(tdt).contiguous()
 
 

@@ -86,6 +86,15 @@ int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
             int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream);
 
 /*
+ * Forward pass with fp16 (IEEE half) q, k, v, o: the same kernel on fp16 matrix
+ * cores, probabilities rounded to fp16 and o stored in fp16, both round to
+ * nearest even (the fp16 store of the Triton page's kernel, section
+ * "流式注意力核心内核").  Same arguments and rules as fa2_fwd.
+ */
+int fa2_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream);
+
+/*
  * Forward pass with fp32 q, k, v, o: fp32 matrix-core products and fp32 state
  * throughout (no reduced-precision step).  Same arguments and rules as fa2_fwd.
  */
@@ -216,6 +225,15 @@ int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts
 int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
             void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward pass of fa2_fwd_f16: fp16 q, k, v, o, dout, dq, dk, dv (fp16 matrix
+ * cores, P and dS rounded to fp16, outputs fp16, round to nearest even).  Same
+ * arguments and rules as fa2_bwd.
+ */
+int fa2_bwd_f16(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Backward pass of fa2_fwd_window: the gradients of attention over the key

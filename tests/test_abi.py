@@ -20,11 +20,11 @@ def header_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert header_functions() == sorted(["fa2_fwd", "fa2_fwd_f32", "fa2_status_string", "fa2_check_args",
+    assert header_functions() == sorted(["fa2_fwd", "fa2_fwd_f16", "fa2_fwd_f32", "fa2_status_string", "fa2_check_args",
                                          "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
                                          "fa2_splitkv_num_splits", "fa2_merge_partials",
                                          "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd_window",
-                                         "fa2_bwd_window"])
+                                         "fa2_bwd_window", "fa2_bwd_f16"])
 
 
 def test_library_exports_every_declared_symbol():
