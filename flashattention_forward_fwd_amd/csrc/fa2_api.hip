@@ -76,7 +76,7 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
 {
     if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
     if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return FA2_ERR_DIM;
-    if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_D;
+    if (d != 32 && d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_D;
     if (causal != 0 && causal != 1) return FA2_ERR_ARG;
     if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_ARG;
     if (elem_bytes != 2 && elem_bytes != 4) return FA2_ERR_ARG;
@@ -262,7 +262,7 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
 
 int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal)
 {
-    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || (d != 64 && d != 128)) return 1;
+    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || (d != 32 && d != 64 && d != 128)) return 1;
     return auto_splits(B, H, Lq, Lk, causal);
 }
 
@@ -320,7 +320,7 @@ int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts
     if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL;
     if (n_parts < 1 || n_parts > FA2_MAX_SPLITS) return FA2_ERR_ARG;
     if (rows < 1) return FA2_ERR_DIM;
-    if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_D;
+    if (d != 32 && d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_D;
     if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
         return FA2_ERR_ALIGN;
     if (!product_fits(n_parts, rows, d, sizeof(float))) return FA2_ERR_DIM;
@@ -389,7 +389,7 @@ const char *fa2_status_string(int status)
     case FA2_OK: return "ok";
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
     case FA2_ERR_DIM: return "B, H, Lq, Lk must be positive and the sizes must fit (one head's K below 2 GiB)";
-    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 64 or 128";
+    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128";
     case FA2_ERR_ARG: return "causal must be 0 or 1 and scale finite and positive";
     case FA2_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";

@@ -78,14 +78,17 @@ constexpr int kRowTile = 64;                      // dK/dV: query rows per LDS t
 //  * ds_read_b64_tr_b16 of 4 consecutive rows x 4 consecutive logical chunks
 //    (the transposed A operand): the 4 rows land in 4 different aligned groups
 //    of 4 chunks, so the 16 (row, chunk) pairs are 16 different chunks.
-// For d = 64 two rows share one 256-byte line; the row parity separates them.
+// For d = 64 two rows, for d = 32 four rows share one 256-byte line; the row
+// within the line separates them.
 template <int D> struct BTile {
     static constexpr int kRowBytes = 2 * D;
     static constexpr int kChunks = kRowBytes / 16;
     static constexpr int kRowsPerXfer = 1024 / kRowBytes;   // rows per 1 KiB DMA transfer
     static __device__ __forceinline__ int swz(int r)
     {
-        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+             : D == 64  ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
+                        : ((r >> 2) & 3);
     }
     // Byte address in the tile of logical byte x of row r.
     static __device__ __forceinline__ int addr(int r, int x)
@@ -104,10 +107,12 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t src, int row0, 
 {
     using T = BTile<D>;
     constexpr int kXfers = ROWS * T::kRowBytes / 1024;
-    static_assert(kXfers % NWAVES == 0, "tile must split evenly over the wavefronts");
+    static_assert(kXfers % NWAVES == 0 || NWAVES % kXfers == 0, "tile must split evenly over the wavefronts");
+    constexpr int kPerWave = kXfers >= NWAVES ? kXfers / NWAVES : 1;
+    if (kXfers < NWAVES && wave >= kXfers) return;    // small tile: the first waves copy it
 #pragma unroll
-    for (int x = 0; x < kXfers / NWAVES; ++x) {
-        const int b = wave * (kXfers / NWAVES) + x;
+    for (int x = 0; x < kPerWave; ++x) {
+        const int b = wave * kPerWave + x;
         const int r = b * T::kRowsPerXfer + lane / T::kChunks;
         const int phys = lane % T::kChunks;
         // The whole offset goes in the VGPR operand, which the range check covers.
@@ -587,16 +592,18 @@ hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
-    return d == 64 ? launch_bwd_d<64, __bf16>(p, masked, rows, o, lse, stream)
-                   : launch_bwd_d<128, __bf16>(p, masked, rows, o, lse, stream);
+    hipError_t err = hipSuccess;
+    with_head_dim(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, __bf16>(p, masked, rows, o, lse, stream); });
+    return err;
 }
 
 hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream)
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
-    return d == 64 ? launch_bwd_d<64, _Float16>(p, masked, rows, o, lse, stream)
-                   : launch_bwd_d<128, _Float16>(p, masked, rows, o, lse, stream);
+    hipError_t err = hipSuccess;
+    with_head_dim(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, _Float16>(p, masked, rows, o, lse, stream); });
+    return err;
 }
 
 }  // namespace fa2

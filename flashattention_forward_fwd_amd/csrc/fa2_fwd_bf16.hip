@@ -74,23 +74,26 @@ template <int D> struct Tile {
     static constexpr int kXfersPerWave = kBc * kRowBytes / 1024 / kWaves;
     static constexpr int kBytes = kBc * kRowBytes;
     // K swizzle repeats every kKPeriod transfers (see swz_k).
-    static constexpr int kKPeriod = D == 128 ? 4 : 2;
+    static constexpr int kKPeriod = D == 128 ? 4 : D == 64 ? 2 : 1;
     static constexpr int kElems = kBc * D;                   // elements per tile
     static_assert(kXfersPerWave * kWaves * 1024 == kBc * kRowBytes, "tile must split into 1 KiB transfers");
 
     // K: chunk q of row r is stored at chunk q ^ swz_k(r).  The score MFMA reads
     // the same logical chunk from 32 consecutive rows; this spreads any 256
-    // consecutive bytes of those reads over all 64 banks.
+    // consecutive bytes of those reads over all 64 banks (d = 64: two rows, and
+    // d = 32: four rows, share a 256-byte line; the row within the line already
+    // separates them, the swizzle separates the lines).
     static __device__ __forceinline__ int swz_k(int r)
     {
-        return D == 128 ? (r & 15) : ((r >> 1) & 7);
+        return D == 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
     }
     // V: the transposing read takes 64 consecutive bytes (4 chunks) from each of
     // 4 consecutive rows; moving each row's 4-chunk group to a different
-    // 64-byte bank group keeps those 4 rows conflict-free.
+    // 64-byte bank group keeps those 4 rows conflict-free (d = 32: the 4 rows
+    // are one 256-byte line already).
     static __device__ __forceinline__ int swz_v(int r)
     {
-        return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+        return D == 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
     }
 };
 
@@ -543,17 +546,15 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         p.lse[(size_t)bh * p.Lq + qrow] = (m + __builtin_amdgcn_logf(l)) * kLn2;
 }
 
-template <bool SPLIT>
+template <bool SPLIT, typename E = __bf16>
 hipError_t launch(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    if (d == 64) {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, true, SPLIT>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, false, SPLIT>), grid, block, 0, stream, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, true, SPLIT>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, false, SPLIT>), grid, block, 0, stream, p);
-    }
+    with_head_dim(d, [&](auto dim) {
+        constexpr int D = decltype(dim)::value;
+        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, SPLIT, false, E>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, SPLIT, false, E>), grid, block, 0, stream, p);
+    });
     return hipGetLastError();
 }
 
@@ -571,22 +572,16 @@ hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStre
 
 hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
-    const dim3 grid(p.n_wg), block(kThreads);
-    if (d == 64) {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, true, false, false, _Float16>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, false, false, false, _Float16>), grid, block, 0, stream, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, true, false, false, _Float16>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, false, false, false, _Float16>), grid, block, 0, stream, p);
-    }
-    return hipGetLastError();
+    return launch<false, _Float16>(p, d, causal, stream);
 }
 
 hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    if (d == 64) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<64, false, false, true>), grid, block, 0, stream, p);
-    else         hipLaunchKernelGGL((fa2_fwd_bf16_kernel<128, false, false, true>), grid, block, 0, stream, p);
+    with_head_dim(d, [&](auto dim) {
+        constexpr int D = decltype(dim)::value;
+        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, stream, p);
+    });
     return hipGetLastError();
 }
 

@@ -177,13 +177,11 @@ void fa2_fwd_f32_kernel(FwdParams p)
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    if (d == 64) {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_f32_kernel<64, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_f32_kernel<64, false>), grid, block, 0, stream, p);
-    } else {
-        if (causal) hipLaunchKernelGGL((fa2_fwd_f32_kernel<128, true>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_f32_kernel<128, false>), grid, block, 0, stream, p);
-    }
+    with_head_dim(d, [&](auto dim) {
+        constexpr int D = decltype(dim)::value;
+        if (causal) hipLaunchKernelGGL((fa2_fwd_f32_kernel<D, true>), grid, block, 0, stream, p);
+        else        hipLaunchKernelGGL((fa2_fwd_f32_kernel<D, false>), grid, block, 0, stream, p);
+    });
     return hipGetLastError();
 }
 

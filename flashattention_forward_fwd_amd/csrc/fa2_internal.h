@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa2 {
 
 // Everything a forward kernel needs; passed by value as the kernel argument.
@@ -110,6 +112,15 @@ __device__ __forceinline__ float halves_sum(float x)
 
 // Host-side launchers (one per element type), defined next to their kernels.
 namespace fa2 {
+// Calls f(std::integral_constant<int, D>{}) for the head dimension d (32, 64 or
+// 128; the entry points reject every other value before a launch).
+template <typename F>
+inline void with_head_dim(int d, F f)
+{
+    if (d == 32) f(std::integral_constant<int, 32>{});
+    else if (d == 64) f(std::integral_constant<int, 64>{});
+    else f(std::integral_constant<int, 128>{});
+}
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t stream);

@@ -52,11 +52,11 @@ def test_argument_checks(elem):
         return fa.fa2_check_args(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Lq"],
                                  a["Lk"], a["d"], a["scale"], a["causal"], elem)
     assert st() == 0
-    assert st(d=64) == 0
+    assert st(d=64) == 0 and st(d=32) == 0 and st(d=128) == 0
     assert st(q=0) == 1 and st(lse=0) == 1 and st(v=0) == 1
     assert st(B=0) == 2 and st(H=-1) == 2 and st(Lq=0) == 2 and st(Lk=0) == 2
     assert st(B=1 << 30, H=1 << 30) == 2
-    for d in (0, 32, 96, 256, 127):
+    for d in (0, 16, 96, 256, 127):
         assert st(d=d) == 3
     assert st(causal=2) == 4 and st(causal=-1) == 4
     assert st(scale=0.0) == 4 and st(scale=-1.0) == 4

@@ -58,6 +58,8 @@ SHAPES = [
     (1, 1, 200, 500, 128),
     (1, 1, 500, 200, 64),
     (2, 2, 384, 384, 128),
+    (1, 2, 129, 129, 32),
+    (1, 1, 300, 200, 32),
 ]
 
 

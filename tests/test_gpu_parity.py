@@ -56,6 +56,9 @@ SHAPES = [
     (1, 2, 1000, 77, 128),
     (1, 1, 384, 384, 64),
     (1, 1, 500, 500, 128),
+    (1, 2, 129, 129, 32),
+    (2, 1, 300, 257, 32),
+    (1, 1, 1, 1, 32),
 ]
 
 
@@ -67,6 +70,15 @@ def test_parity_ragged(shape, causal, dtype):
     q, k, v = random_qkv(B, H, Lq, Lk, d, dtype, seed=sum(shape) + 7 * causal)
     scale = float(np.float32(1.0) / np.sqrt(np.float32(d)))
     check_case("ragged %s %s" % (shape, dtype), q, k, v, causal, scale, dtype)
+
+
+def test_pages_selfcheck_recipe_through_kernel():
+    """The pages' NumPy self-check recipe (rng(0) normal, 100 x 32 for Q, K, V): the
+    same draws, rounded to bf16 (and kept fp32), through the kernels."""
+    Q, K, V = np.random.default_rng(0).normal(size=(3, 100, 32))
+    for dtype, tdt in (("bf16", torch.bfloat16), ("fp32", torch.float32)):
+        q, k, v = (torch.from_numpy(x[None, None].astype(np.float32)).to(tdt) for x in (Q, K, V))
+        check_case("pages' self-check recipe", q, k, v, False, float(np.float32(1 / np.sqrt(32))), dtype)
 
 
 @pytest.mark.parametrize("causal", [False, True])

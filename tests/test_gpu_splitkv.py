@@ -33,6 +33,7 @@ SHAPES = [
     (1, 2, 1000, 77, 128),
     (1, 1, 500, 500, 128),
     (1, 2, 300, 5000, 128),
+    (1, 2, 200, 700, 32),
 ]
 
 
@@ -130,7 +131,7 @@ def test_splitkv_workspace_too_small():
 
 
 # ------------------------------------------------------ stand-alone merge kernel
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [32, 64, 128])
 def test_merge_partials_matches_oracle(d):
     """Partials: the oracle's attention over key shards (rounded to fp32), plus one
     part that is empty (-inf, NaN output) for every row and one empty for some rows."""

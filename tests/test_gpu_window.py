@@ -47,6 +47,7 @@ CASES = [
     (1, 1, 640, 640, 64, 127, -1),
     (2, 1, 384, 384, 128, 200, 200),
     (1, 1, 129, 1000, 128, 5, 900),
+    (1, 2, 300, 300, 32, 20, 0),
 ]
 
 
@@ -91,6 +92,7 @@ BWD_CASES = [
     (1, 1, 333, 333, 128, 0, 0),
     (1, 2, 384, 512, 128, -1, 50),
     (1, 1, 640, 640, 64, 127, -1),
+    (1, 2, 300, 300, 32, 20, 3),
 ]
 
 
