@@ -70,13 +70,17 @@ bool product_fits(int64_t a, int64_t b, int64_t c, int64_t d)
     return a <= lim / d;
 }
 
+// Head dimensions of the 16-bit forward kernels (and the merge), and of the
+// fp32 forward and the backward kernels.
+bool head_dim_ok(int d, bool with_256) { return d == 32 || d == 64 || d == 128 || (with_256 && d == 256); }
+
 int prepare(const void *q, const void *k, const void *v, const void *o, const float *lse,
             int B, int H, int Lq, int Lk, int d, float scale, int causal, int elem_bytes,
-            fa2::FwdParams *out)
+            fa2::FwdParams *out, bool with_256 = false)
 {
     if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
     if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return FA2_ERR_DIM;
-    if (d != 32 && d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_D;
+    if (!head_dim_ok(d, with_256)) return FA2_ERR_UNSUPPORTED_D;
     if (causal != 0 && causal != 1) return FA2_ERR_ARG;
     if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_ARG;
     if (elem_bytes != 2 && elem_bytes != 4) return FA2_ERR_ARG;
@@ -205,14 +209,14 @@ extern "C" {
 int fa2_check_args(const void *q, const void *k, const void *v, const void *o, const float *lse,
                    int B, int H, int Lq, int Lk, int d, float scale, int causal, int elem_bytes)
 {
-    return prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes, nullptr);
+    return prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes, nullptr, elem_bytes == 2);
 }
 
 int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
             int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, true);
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     if (fa2::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -224,7 +228,7 @@ int fa2_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, true);
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     if (fa2::launch_fwd_f16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -249,7 +253,7 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
                    void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 2, &p);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 2, &p, true);
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     // Negative bounds all mean "unbounded"; keep them as -1.
@@ -262,7 +266,7 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
 
 int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal)
 {
-    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || (d != 32 && d != 64 && d != 128)) return 1;
+    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || !head_dim_ok(d, true)) return 1;
     return auto_splits(B, H, Lq, Lk, causal);
 }
 
@@ -271,7 +275,7 @@ size_t fa2_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int caus
     // Size checks of fa2_fwd_splitkv, on stand-in aligned pointers.
     const void *fake = reinterpret_cast<const void *>(uintptr_t(256));
     if (prepare(fake, fake, fake, fake, static_cast<const float *>(fake), B, H, Lq, Lk, d, 1.0f,
-                causal, 2, nullptr) != FA2_OK)
+                causal, 2, nullptr, true) != FA2_OK)
         return 0;
     if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return 0;
     const int S = num_splits == 0 ? auto_splits(B, H, Lq, Lk, causal) : num_splits;
@@ -283,7 +287,7 @@ int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float 
                     int num_splits, void *workspace, size_t workspace_bytes_given, void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, true);
     if (st != FA2_OK) return st;
     if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return FA2_ERR_ARG;
     if (!workspace) return FA2_ERR_WORKSPACE;
@@ -320,7 +324,7 @@ int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts
     if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL;
     if (n_parts < 1 || n_parts > FA2_MAX_SPLITS) return FA2_ERR_ARG;
     if (rows < 1) return FA2_ERR_DIM;
-    if (d != 32 && d != 64 && d != 128) return FA2_ERR_UNSUPPORTED_D;
+    if (!head_dim_ok(d, true)) return FA2_ERR_UNSUPPORTED_D;
     if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
         return FA2_ERR_ALIGN;
     if (!product_fits(n_parts, rows, d, sizeof(float))) return FA2_ERR_DIM;
@@ -389,7 +393,7 @@ const char *fa2_status_string(int status)
     case FA2_OK: return "ok";
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
     case FA2_ERR_DIM: return "B, H, Lq, Lk must be positive and the sizes must fit (one head's K below 2 GiB)";
-    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128";
+    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128 (or 256 for the 16-bit forward)";
     case FA2_ERR_ARG: return "causal must be 0 or 1 and scale finite and positive";
     case FA2_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";

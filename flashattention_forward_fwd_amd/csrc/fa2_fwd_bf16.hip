@@ -73,19 +73,24 @@ template <int D> struct Tile {
     static constexpr int kRowsPerXfer = 1024 / kRowBytes;    // rows per 1 KiB wave transfer
     static constexpr int kXfersPerWave = kBc * kRowBytes / 1024 / kWaves;
     static constexpr int kBytes = kBc * kRowBytes;
-    // K swizzle repeats every kKPeriod transfers (see swz_k).
-    static constexpr int kKPeriod = D == 128 ? 4 : D == 64 ? 2 : 1;
+    // K swizzle repeats every kKPeriod transfers (see swz_k), V swizzle every
+    // kVPeriod (d = 256: a transfer holds two rows, the V swizzle spans four).
+    static constexpr int kKPeriod = D == 256 ? 8 : D == 128 ? 4 : D == 64 ? 2 : 1;
+    static constexpr int kVPeriod = D == 256 ? 2 : 1;
     static constexpr int kElems = kBc * D;                   // elements per tile
     static_assert(kXfersPerWave * kWaves * 1024 == kBc * kRowBytes, "tile must split into 1 KiB transfers");
+    static_assert(kXfersPerWave % kKPeriod == 0 && kXfersPerWave % kVPeriod == 0,
+                  "a wave's transfers must start at a swizzle period");
 
     // K: chunk q of row r is stored at chunk q ^ swz_k(r).  The score MFMA reads
     // the same logical chunk from 32 consecutive rows; this spreads any 256
     // consecutive bytes of those reads over all 64 banks (d = 64: two rows, and
     // d = 32: four rows, share a 256-byte line; the row within the line already
-    // separates them, the swizzle separates the lines).
+    // separates them, the swizzle separates the lines; d = 256: each row spans
+    // two lines, the swizzle moves the chunk within the row's first 16).
     static __device__ __forceinline__ int swz_k(int r)
     {
-        return D == 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+        return D >= 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
     }
     // V: the transposing read takes 64 consecutive bytes (4 chunks) from each of
     // 4 consecutive rows; moving each row's 4-chunk group to a different
@@ -93,7 +98,7 @@ template <int D> struct Tile {
     // are one 256-byte line already).
     static __device__ __forceinline__ int swz_v(int r)
     {
-        return D == 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
+        return D >= 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
     }
 };
 
@@ -104,10 +109,10 @@ constexpr int kRawBufferFlags = 0x00020000;
 // 1 KiB block b = w * kXfersPerWave + x of the tile; lane l lands at byte 16 l
 // of the block, i.e. row b * kRowsPerXfer + l / kChunks, physical chunk
 // l % kChunks, and reads that row's logical chunk.  The K swizzle depends on
-// b % kKPeriod, the V swizzle only on the lane.
+// b % kKPeriod, the V swizzle on b % kVPeriod.
 template <int D> struct LoadOffsets {
     int k[Tile<D>::kKPeriod];
-    int v;
+    int v[Tile<D>::kVPeriod];
 };
 
 template <int D>
@@ -121,8 +126,11 @@ __device__ __forceinline__ LoadOffsets<D> load_offsets(int lane)
         const int row = b * T::kRowsPerXfer + lane / T::kChunks;
         o.k[b] = row * T::kRowBytes + 16 * (phys ^ T::swz_k(row));
     }
-    const int row = lane / T::kChunks;
-    o.v = row * T::kRowBytes + 16 * (phys ^ T::swz_v(row));
+#pragma unroll
+    for (int b = 0; b < T::kVPeriod; ++b) {
+        const int row = b * T::kRowsPerXfer + lane / T::kChunks;
+        o.v[b] = row * T::kRowBytes + 16 * (phys ^ T::swz_v(row));
+    }
     return o;
 }
 
@@ -137,8 +145,8 @@ __device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t src, int 
 #pragma unroll
     for (int x = 0; x < T::kXfersPerWave; ++x) {
         const int b = wave * T::kXfersPerWave + x;
-        const int voff = IS_V ? off.v : off.k[x % T::kKPeriod];
-        const int soff = tile * T::kBytes + (IS_V ? b : b - b % T::kKPeriod) * 1024;
+        const int voff = IS_V ? off.v[x % T::kVPeriod] : off.k[x % T::kKPeriod];
+        const int soff = tile * T::kBytes + (IS_V ? b - b % T::kVPeriod : b - b % T::kKPeriod) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void *)(dst + b * 512), 16, voff, soff, 0, 0);
     }
 }
@@ -310,12 +318,15 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
 // query tile's K/V tiles and writes the fp32 partial O (normalised by its own
 // row sum) and partial LSE of that range; rows that see no key of the range
 // get LSE = -inf and no O.  Otherwise it covers all tiles and writes bf16 O.
+// D = 256: the Q fragment (64 VGPRs) and the O accumulators (128) leave no room
+// for two wavefronts per SIMD, so that instance runs one wavefront per SIMD with
+// the accumulation registers in use (and one work-group per CU: 128 KiB of LDS).
 // WINDOW (with CAUSAL and SPLIT false): key j is visible to query i iff
 // (p.wl < 0 or j >= i - p.wl) and (p.wr < 0 or j <= i + p.wr); the work-group
 // visits only the tiles that hold a key visible to one of its rows, and a row
 // that sees no key gets O = 0 and LSE = -inf.
 template <int D, bool CAUSAL, bool SPLIT, bool WINDOW = false, typename E = __bf16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
 {
     using T = Tile<D>;
@@ -550,7 +561,7 @@ template <bool SPLIT, typename E = __bf16>
 hipError_t launch(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    with_head_dim(d, [&](auto dim) {
+    with_head_dim<true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, SPLIT, false, E>), grid, block, 0, stream, p);
         else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, SPLIT, false, E>), grid, block, 0, stream, p);
@@ -578,7 +589,7 @@ hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t st
 hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    with_head_dim(d, [&](auto dim) {
+    with_head_dim<true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, stream, p);
     });

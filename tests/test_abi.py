@@ -56,8 +56,9 @@ def test_argument_checks(elem):
     assert st(q=0) == 1 and st(lse=0) == 1 and st(v=0) == 1
     assert st(B=0) == 2 and st(H=-1) == 2 and st(Lq=0) == 2 and st(Lk=0) == 2
     assert st(B=1 << 30, H=1 << 30) == 2
-    for d in (0, 16, 96, 256, 127):
+    for d in (0, 16, 96, 512, 127):
         assert st(d=d) == 3
+    assert st(d=256) == (0 if elem == 2 else 3)      # d = 256: 16-bit forward only
     assert st(causal=2) == 4 and st(causal=-1) == 4
     assert st(scale=0.0) == 4 and st(scale=-1.0) == 4
     assert st(scale=float("inf")) == 4 and st(scale=float("nan")) == 4
@@ -173,3 +174,13 @@ def test_window_rejects_before_touching_the_device():
     assert f(A, A, A, A, A, 1, 1, 0, 8, 64, 0.1, 4, 0, None) == 2
     assert f(A, A, A, A, A, 1, 1, 8, 8, 64, float("nan"), 4, 0, None) == 4
     assert f(A, A, A, A, A + 4, 1, 1, 8, 8, 64, 0.1, 4, 0, None) == 5
+
+
+def test_head_dim_256_only_for_16bit_forward():
+    L = fa.lib()
+    big = 1 << 30
+    args = [A] * 9
+    assert L.fa2_bwd(*args, 1, 1, 8, 8, 256, 0.1, 0, A, big, None) == 3
+    assert L.fa2_fwd_f32(A, A, A, A, A, 1, 1, 8, 8, 256, 0.1, 0, None) == 3
+    assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 256, 0, 2) > 0
+    assert fa.lib().fa2_merge_partials(A, A, 2, 10, 256, A, A + 4, None) == 5

@@ -72,6 +72,16 @@ def test_parity_ragged(shape, causal, dtype):
     check_case("ragged %s %s" % (shape, dtype), q, k, v, causal, scale, dtype)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 200, 300, 256), (2, 1, 129, 129, 256), (1, 1, 1, 70, 256)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_parity_head_dim_256(shape, causal):
+    """d = 256 (bf16 only: the one-wavefront-per-SIMD instance)."""
+    B, H, Lq, Lk, d = shape
+    q, k, v = random_qkv(B, H, Lq, Lk, d, "bf16", seed=sum(shape) + 5 * causal)
+    check_case("d256 %s" % (shape,), q, k, v, causal, float(np.float32(1 / np.sqrt(d))), "bf16")
+
+
 def test_pages_selfcheck_recipe_through_kernel():
     """The pages' NumPy self-check recipe (rng(0) normal, 100 x 32 for Q, K, V): the
     same draws, rounded to bf16 (and kept fp32), through the kernels."""

@@ -48,6 +48,7 @@ CASES = [
     (2, 1, 384, 384, 128, 200, 200),
     (1, 1, 129, 1000, 128, 5, 900),
     (1, 2, 300, 300, 32, 20, 0),
+    (1, 1, 300, 400, 256, 50, 10),
 ]
 
 
