@@ -7,7 +7,7 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRCS = [os.path.join(HERE, n) for n in ("attn_ref.c", "attn_bwd_ref.c", "attn_window_ref.c")]
+SRCS = [os.path.join(HERE, n) for n in ("attn_ref.c", "attn_bwd_ref.c", "attn_window_ref.c", "attn_dropout_ref.c")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 

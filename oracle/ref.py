@@ -17,6 +17,10 @@ Three references, each a plain reading of the pages:
   reaches the definition's result.
 * ``attention_window_f64`` -- the definition restricted to a window of keys around
   each query (sliding-window / local attention), computed by ``attn_window_ref.c``.
+* ``philox4x32_10`` / ``dropout_mask`` / ``attention_dropout_f64`` -- the counter-based
+  generator of the SC'11 Philox paper, the dropout keep mask drawn from it, and
+  attention with dropout on the probabilities (forward and gradients), computed by
+  ``attn_dropout_ref.c``.
 * ``attention_bwd_f64`` -- the gradients dQ, dK, dV of the definition (the
   backward pass), by the chain rule, computed by ``attn_bwd_ref.c``.
 * ``merge_partials`` -- the combine of attention results over disjoint key sets
@@ -61,6 +65,18 @@ def _lib():
             ctypes.c_double, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.oracle_philox4x32_10.restype = None
+        lib.oracle_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        lib.oracle_dropout_mask.restype = ctypes.c_int
+        lib.oracle_dropout_mask.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, ctypes.c_void_p]
+        lib.oracle_attention_dropout_f64.restype = ctypes.c_int
+        lib.oracle_attention_dropout_f64.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_double, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.oracle_attention_bwd_window_f64.restype = ctypes.c_int
         lib.oracle_attention_bwd_window_f64.argtypes = [
@@ -333,3 +349,70 @@ def merge_partials(o_parts, lse_parts):
         o = w1[..., None] * o + w2[..., None] * o2
         lse = l_new
     return o, lse
+
+
+def dropout_threshold(p):
+    """Keep threshold t = round(256 (1 - p)) in 1..256: a byte u keeps iff u < t, so the
+    keep probability is t / 256 and kept values are scaled by 256 / t."""
+    if not (0.0 <= p < 1.0):
+        raise ValueError("dropout probability must be in [0, 1)")
+    return int(min(256, max(1, round(256.0 * (1.0 - p)))))
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) of a 4-word counter and
+    2-word key (uint32 each); returns the 4 output words."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k_ = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, dtype=np.uint32)
+    assert c.shape == (4,) and k_.shape == (2,)
+    _lib().oracle_philox4x32_10(c.ctypes.data, k_.ctypes.data, out.ctypes.data)
+    return out
+
+
+def dropout_mask(B, H, Lq, Lk, seed, offset, t):
+    """Keep mask [B, H, Lq, Lk] (bool) of the dropout reading: byte (j % 4) of word
+    (i % 4) of Philox4x32-10 at counter (j / 4, i / 4, b H + h, offset), key
+    (seed low, seed high), kept iff below t."""
+    m = np.empty((B, H, Lq, Lk), dtype=np.uint8)
+    rc = _lib().oracle_dropout_mask(B, H, Lq, Lk, int(seed), int(offset), int(t), m.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_dropout_mask rejected its arguments (code %d)" % rc)
+    return m.astype(bool)
+
+
+def attention_dropout_f64(q, k, v, scale, causal, seed, offset, t, dout=None, nthreads=None):
+    """Attention with dropout on the probabilities, in float64, by definition.
+
+    A = P * mask * 256 / t (mask from ``dropout_mask``), O = A V; lse is the
+    logsumexp of the scores without dropout.  With dout, also the gradients:
+    dV = A^T dO, dA = dO V^T, dP = dA * mask * 256 / t, D = rowsum(A * dA),
+    dS = P (dP - D), dQ = scale dS K, dK = scale dS^T Q.  The pages list dropout
+    among the steps fused into one pass over a score block ("Flash Attention
+    全解析（上）" section 2.1.2) without a formula; the mask, threshold and scale
+    are this project's reading.  Returns (o, lse) or (o, lse, dq, dk, dv).
+    Holds P for every (row, key): small sizes only.
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    o = np.empty((B, H, Lq, d))
+    lse = np.empty((B, H, Lq))
+    grads = None
+    dptr = None
+    if dout is not None:
+        dout = np.ascontiguousarray(dout, dtype=np.float64)
+        grads = (np.empty((B, H, Lq, d)), np.empty((B, H, Lk, d)), np.empty((B, H, Lk, d)))
+        dptr = dout.ctypes.data
+    if nthreads is None:
+        nthreads = default_threads()
+    rc = _lib().oracle_attention_dropout_f64(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, dptr, B, H, Lq, Lk, d, float(scale), int(bool(causal)),
+        int(seed), int(offset), int(t), o.ctypes.data, lse.ctypes.data,
+        grads[0].ctypes.data if grads else None, grads[1].ctypes.data if grads else None,
+        grads[2].ctypes.data if grads else None, int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attention_dropout_f64 rejected its arguments (code %d)" % rc)
+    return (o, lse) if grads is None else (o, lse) + grads
