@@ -13,17 +13,17 @@ import math
 from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_f16, fa2_bwd_window,  # noqa: F401
                    fa2_bwd_workspace_bytes,
                    fa2_check_args, fa2_fwd, fa2_fwd_f16, fa2_fwd_f32, fa2_fwd_splitkv, fa2_fwd_window,
-                   fa2_merge_partials,
+                   fa2_fwd_dropout, fa2_merge_partials,
                    fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib, status_string)
 
 __all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f16", "fa2_fwd_f32", "fa2_fwd_splitkv",
            "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
-           "fa2_fwd_window", "fa2_bwd", "fa2_bwd_f16", "fa2_bwd_window", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
+           "fa2_fwd_window", "fa2_fwd_dropout", "fa2_bwd", "fa2_bwd_f16", "fa2_bwd_window", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
            "FA2_MAX_SPLITS"]
 
 
 def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, workspace=None,
-            window=None):
+            window=None, dropout=None):
     """O = softmax(scale * Q K^T [causal]) V and the per-row logsumexp.
 
     q: [B, H, Lq, d], k and v: [B, H, Lk, d], all bf16, all fp16 or all fp32 CUDA tensors
@@ -38,6 +38,11 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
     window (bf16 only): (window_left, window_right) runs ``fa2_fwd_window`` --
     key j visible to query i iff i - window_left <= j <= i + window_right, a
     negative bound meaning unbounded; causal must then be False.
+
+    dropout (bf16 only): (p, seed, offset) runs ``fa2_fwd_dropout`` -- each
+    probability kept with probability round(256 (1 - p)) / 256 by the Philox
+    keep mask of (seed, offset), kept ones scaled up by the inverse; lse is the
+    one without dropout.  Pass the same tuple to ``backward``.
     """
     import torch
 
@@ -60,6 +65,13 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     c = int(bool(causal))
+    if dropout is not None:
+        if q.dtype != torch.bfloat16 or window is not None or num_splits is not None:
+            raise ValueError("dropout takes bfloat16 tensors, no window and no num_splits")
+        p_drop, seed, offset = dropout
+        fa2_fwd_dropout(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, float(p_drop), int(seed), int(offset),
+                        stream)
+        return out, lse
     if window is not None:
         if q.dtype != torch.bfloat16 or causal or num_splits is not None:
             raise ValueError("window takes bfloat16 tensors, causal=False and no num_splits")

@@ -23,6 +23,9 @@ _I = ctypes.c_int
 _F = ctypes.c_float
 _Z = ctypes.c_size_t
 _L = ctypes.c_int64
+_D = ctypes.c_double
+_U64 = ctypes.c_uint64
+_U32 = ctypes.c_uint32
 SIGNATURES = {
     "fa2_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa2_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -34,6 +37,7 @@ SIGNATURES = {
     "fa2_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fa2_merge_partials": (_I, [_P, _P, _I, _L, _I, _P, _P, _P]),
     "fa2_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa2_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _D, _U64, _U32, _P]),
     "fa2_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa2_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
     "fa2_bwd_f16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
@@ -174,6 +178,15 @@ def fa2_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_
                               int(window_left), int(window_right), _ptr(stream))
     if st != FA2_OK:
         raise FA2Error(st, "fa2_fwd_window")
+
+
+def fa2_fwd_dropout(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset, stream):
+    """libfa2 ``fa2_fwd_dropout`` (bf16, Philox keep mask of (seed, offset)).  Raises FA2Error."""
+    st = lib().fa2_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                               float(dropout_p), int(seed), int(offset), _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_fwd_dropout")
 
 
 def fa2_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, window_left, window_right,

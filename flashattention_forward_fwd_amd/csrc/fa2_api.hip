@@ -103,7 +103,24 @@ int prepare(const void *q, const void *k, const void *v, const void *o, const fl
         out->n_wg = (int)(n_qtiles * B * H);
         out->wl = -1;
         out->wr = causal ? 0 : -1;
+        out->drop = fa2::DropoutParams{0u, 0u, 0u, 256u, 1.0f};
     }
+    return FA2_OK;
+}
+
+// Dropout settings: keep threshold t = round(256 (1 - p)) (ties to even) in
+// 1..256, scale 256 / t.  p must lie in [0, 1).
+int dropout_setup(double p_drop, uint64_t seed, uint32_t offset, fa2::DropoutParams *dp)
+{
+    if (!(p_drop >= 0.0 && p_drop < 1.0)) return FA2_ERR_ARG;
+    double t = nearbyint(256.0 * (1.0 - p_drop));
+    if (t < 1.0) t = 1.0;
+    if (t > 256.0) t = 256.0;
+    dp->seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+    dp->seed_hi = (uint32_t)(seed >> 32);
+    dp->offset = offset;
+    dp->threshold = (uint32_t)t;
+    dp->keep_scale = (float)(256.0 / t);
     return FA2_OK;
 }
 
@@ -198,6 +215,7 @@ int prepare_bwd(const void *q, const void *k, const void *v, const void *o, cons
         out->n_wg = 0;
         out->wl = -1;
         out->wr = causal ? 0 : -1;
+        out->drop = fa2::DropoutParams{0u, 0u, 0u, 256u, 1.0f};
     }
     return FA2_OK;
 }
@@ -260,6 +278,20 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
     p.wl = window_left < 0 ? -1 : window_left;
     p.wr = window_right < 0 ? -1 : window_right;
     if (fa2::launch_fwd_bf16_window(p, d, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                    double dropout_p, uint64_t seed, uint32_t offset, void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, true);
+    if (st != FA2_OK) return st;
+    if ((st = dropout_setup(dropout_p, seed, offset, &p.drop)) != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (fa2::launch_fwd_bf16_dropout(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
         return FA2_ERR_LAUNCH;
     return FA2_OK;
 }

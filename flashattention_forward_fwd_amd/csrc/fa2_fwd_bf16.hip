@@ -231,10 +231,39 @@ __device__ __forceinline__ float reference_max(float m)
     return (EMPTY_ROWS && m == -INFINITY) ? 0.0f : m;
 }
 
+// Dropout keep bytes of one score tile for this lane: word g of y[t] holds the
+// generator bytes of keys k0 + 32t + 8g + 4hh + 0..3 (byte = key mod 4) of the
+// lane's query.  Those keys form one 4-key block, and the four lanes of a quad
+// (queries 4a .. 4a + 3) share its 4-query block, so lane s of the quad computes
+// the blocks g = s of both t and the quad transpose hands each lane the word of
+// its own query (word = query mod 4; q0 is a multiple of 4).
+struct TileMask {
+    u32x4 y[2];
+};
+
+template <bool DROPOUT>
+__device__ __forceinline__ TileMask tile_mask(const DropoutParams &dp, int k0, int qrow, int lane, int bh)
+{
+    TileMask mk;
+    if (DROPOUT) {
+        const int s = lane & 3, hh = lane >> 5;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t kblock = (uint32_t)(k0 / 4 + 8 * t + 2 * s + hh);
+            mk.y[t] = quad_transpose(philox4x32_10(kblock, (uint32_t)qrow / 4u, (uint32_t)bh, dp.offset,
+                                                   dp.seed_lo, dp.seed_hi), s);
+        }
+    }
+    return mk;
+}
+
 // P~ = 2^(S c - m) as bf16 B operands (one per 16-key chunk: slots 0-3 are keys
 // 16c + 4hh + 0..3, slots 4-7 keys 16c + 8 + 4hh + 0..3), and its row sum.
-template <typename E>
-__device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, float m, typename V16<E>::x8 (&pf)[4])
+// DROPOUT: the row sum is taken before the mask; dropped entries become 0 in the
+// operands (the 1 / keep-rate factor is applied to O at the end).
+template <typename E, bool DROPOUT = false>
+__device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, float m, typename V16<E>::x8 (&pf)[4],
+                                               const TileMask &mk = TileMask{}, uint32_t thr = 256)
 {
     float rs = 0.f;
 #pragma unroll
@@ -245,6 +274,10 @@ __device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, f
         for (int e = 0; e < 8; ++e) {
             v8[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i0 + e], c2, -m));
             rs += v8[e];
+            if (DROPOUT) {
+                const uint32_t u = (mk.y[t][2 * (c & 1) + e / 4] >> (8 * (e % 4))) & 0xFFu;
+                v8[e] = u < thr ? v8[e] : 0.0f;
+            }
         }
         pf[c] = __builtin_convertvector(v8, typename V16<E>::x8);
     }
@@ -284,16 +317,18 @@ __device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, f
 // One step of the pipelined loop for tile j: probabilities of tile j (VALU)
 // while the scores of tile j+1 run (MFMA), then O~ += P~_j V_j (MFMA) while the
 // max of tile j+1 is taken (VALU).
-template <int D, typename E, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW>
+template <int D, typename E, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW, bool DROPOUT>
 __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const LDS_AS char *v_cur,
                                                const typename V16<E>::x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
                                                f32x16 (&s_cur)[2], float &m, float &lpart, float &alpha,
                                                float c2, int j, int t0, int plain_lo, int n_plain, int Lk,
-                                               int qrow, int hh, int k_lane, int v_lane, int wl, int wr)
+                                               int qrow, int hh, int k_lane, int v_lane, int wl, int wr,
+                                               const DropoutParams &dp, int lane, int bh)
 {
     if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
     typename V16<E>::x8 pf[4];
-    const float rs = probabilities<E>(s_cur, c2, reference_max<EMPTY_ROWS>(m), pf);
+    const TileMask mk = tile_mask<DROPOUT>(dp, (t0 + j) * kBc, qrow, lane, bh);
+    const float rs = probabilities<E, DROPOUT>(s_cur, c2, reference_max<EMPTY_ROWS>(m), pf, mk, dp.threshold);
     f32x16 s_next[2];
     scores<D, E>(k_next, qf, s_next, k_lane);
     accumulate_pv<D, E>(v_cur, pf, acc_o, v_lane);
@@ -325,7 +360,10 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
 // (p.wl < 0 or j >= i - p.wl) and (p.wr < 0 or j <= i + p.wr); the work-group
 // visits only the tiles that hold a key visible to one of its rows, and a row
 // that sees no key gets O = 0 and LSE = -inf.
-template <int D, bool CAUSAL, bool SPLIT, bool WINDOW = false, typename E = __bf16>
+// DROPOUT (SPLIT and WINDOW false): each probability is kept iff its generator
+// byte is below p.drop.threshold (the keep mask of tile_mask), and O is scaled by
+// p.drop.keep_scale; m, l and the LSE are those without dropout.
+template <int D, bool CAUSAL, bool SPLIT, bool WINDOW = false, typename E = __bf16, bool DROPOUT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 void fa2_fwd_bf16_kernel(FwdParams p)
 {
@@ -333,6 +371,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     using e8 = typename V16<E>::x8;
     using e4 = typename V16<E>::x4;
     static_assert(!WINDOW || (!CAUSAL && !SPLIT), "the window replaces the causal mask; no split");
+    static_assert(!DROPOUT || (!SPLIT && !WINDOW), "dropout runs in the one-pass forward only");
     // Rows without a visible key in a visited tile range: a causal range that
     // starts after tile 0, or a window (rows at a window edge of the block).
     constexpr bool kEmptyRows = (SPLIT && CAUSAL) || WINDOW;
@@ -483,18 +522,18 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         // even tile j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK0, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
-        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf,
-                                                      acc_o, s_cur, m, lpart, alpha, c2, j, t0, plain_lo, n_plain,
-                                                      p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr);
+        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(
+            (const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+            plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
         __syncthreads();                      // ... everyone's, and the read buffers are free
         if (++j + 1 >= n_wave) break;
         // odd tile j: K_{j+1} in sK0, V_j in sV1; loads K_{j+2} -> sK1, V_{j+1} -> sV0
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK1, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
-        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW>((const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf,
-                                                      acc_o, s_cur, m, lpart, alpha, c2, j, t0, plain_lo, n_plain,
-                                                      p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr);
+        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(
+            (const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+            plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         ++j;
@@ -505,7 +544,8 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         if (j + 1 < n_kv) load_tile_async<D, true>(rV, t0 + j + 1, odd ? sV0 : sV1, wave, loff);
         if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
         e8 pf[4];
-        lpart += probabilities<E>(s_cur, c2, reference_max<kEmptyRows>(m), pf);
+        const TileMask mk = tile_mask<DROPOUT>(p.drop, (t0 + j) * kBc, qrow, lane, bh);
+        lpart += probabilities<E, DROPOUT>(s_cur, c2, reference_max<kEmptyRows>(m), pf, mk, p.drop.threshold);
         accumulate_pv<D, E>((const LDS_AS char *)(odd ? sV1 : sV0), pf, acc_o, v_lane);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -542,7 +582,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     }
     // A window can leave a row without a visible key: O = 0, LSE = -inf.
     const bool seen = !WINDOW || l > 0.0f;
-    const float inv_l = seen ? 1.0f / l : 0.0f;
+    const float inv_l = seen ? (DROPOUT ? p.drop.keep_scale : 1.0f) / l : 0.0f;
     uint16_t *O = static_cast<uint16_t *>(p.o) + ((size_t)bh * p.Lq + qrow) * D;
 #pragma unroll
     for (int dt = 0; dt < kDt; ++dt)
@@ -592,6 +632,19 @@ hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
     with_head_dim<true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, stream, p);
+    });
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16_dropout(const FwdParams &p, int d, bool causal, hipStream_t stream)
+{
+    const dim3 grid(p.n_wg), block(kThreads);
+    with_head_dim<true>(d, [&](auto dim) {
+        constexpr int D = decltype(dim)::value;
+        if (causal)
+            hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, false, false, __bf16, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, false, __bf16, true>), grid, block, 0, stream, p);
     });
     return hipGetLastError();
 }

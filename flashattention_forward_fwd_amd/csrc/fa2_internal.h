@@ -7,6 +7,8 @@
 
 #include <type_traits>
 
+#include "fa2_dropout.h"
+
 namespace fa2 {
 
 // Everything a forward kernel needs; passed by value as the kernel argument.
@@ -23,6 +25,7 @@ struct FwdParams {
     int n_wg;           // n_qtiles * B * H * n_splits
     int wl, wr;         // window kernels: key j visible to query i iff
                         // (wl < 0 or j >= i - wl) and (wr < 0 or j <= i + wr)
+    DropoutParams drop; // dropout kernels: keep mask and scale
 };
 
 // Everything a backward kernel needs (q, k, v, dout bf16 inputs; dq, dk, dv bf16
@@ -44,6 +47,7 @@ struct BwdParams {
     int n_wg;           // n_blocks * B * H
     int wl, wr;         // key j visible to query i iff (wl < 0 or j >= i - wl) and
                         // (wr < 0 or j <= i + wr); causal is (-1, 0), full (-1, -1)
+    DropoutParams drop; // dropout kernels: keep mask and scale
 };
 
 constexpr int kWave = 64;          // CDNA wavefront width
@@ -131,6 +135,8 @@ hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t st
 hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream);
 // Window forward: p.wl, p.wr select the visible keys (bf16, one pass).
 hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream);
+// Dropout forward: p.drop selects the keep mask (bf16, one pass).
+hipError_t launch_fwd_bf16_dropout(const FwdParams &p, int d, bool causal, hipStream_t stream);
 // Backward: D and lse2 into p.delta / p.lse2 from o and lse, then dK/dV, then dQ,
 // for the keys p.wl / p.wr leave visible.
 hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);

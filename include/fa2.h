@@ -125,6 +125,28 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
                    void *stream);
 
 /*
+ * Forward pass with dropout on the attention probabilities, bf16.  "Flash
+ * Attention 全解析（上）", section 2.1.2, lists dropout among the steps fused into
+ * the one pass over a score block, without fixing a generator; this is the reading
+ * adopted:
+ *     o = (P * Z * 256 / t) V,   P = softmax(scale q k^T) (causal mask as fa2_fwd)
+ * with the keep mask Z[b, h, i, j] = [u < t], t = round(256 (1 - dropout_p)) (ties
+ * to even, clamped to 1..256), and u = byte (j mod 4) of output word (i mod 4) of
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) at counter
+ * (j / 4, i / 4, b * H + h, offset) and key (seed & 0xffffffff, seed >> 32).
+ * The keep probability is t / 256 (dropout_p is quantised to multiples of 1/256).
+ * lse is the logsumexp of the scores WITHOUT dropout, as fa2_fwd writes it.  The
+ * same (seed, offset) must be passed to fa2_bwd_dropout for the gradients; a caller
+ * that draws a fresh mask per step changes offset (or seed).
+ *   dropout_p : in [0, 1); 0 keeps everything (o as fa2_fwd, to rounding)
+ * FA2_ERR_ARG also for dropout_p outside [0, 1) or NaN.  Same arguments, precision,
+ * layout and error rules as fa2_fwd otherwise.
+ */
+int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
+                    int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                    double dropout_p, uint64_t seed, uint32_t offset, void *stream);
+
+/*
  * Split-KV forward (FlashDecoding): the same result as fa2_fwd, computed in two
  * stages on `stream` ("Flash Attention 全解析（上）", section 4.3).
  *

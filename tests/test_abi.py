@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
                                          "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
                                          "fa2_splitkv_num_splits", "fa2_merge_partials",
                                          "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd_window",
-                                         "fa2_bwd_window", "fa2_bwd_f16"])
+                                         "fa2_bwd_window", "fa2_bwd_f16", "fa2_fwd_dropout"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -174,6 +174,16 @@ def test_window_rejects_before_touching_the_device():
     assert f(A, A, A, A, A, 1, 1, 0, 8, 64, 0.1, 4, 0, None) == 2
     assert f(A, A, A, A, A, 1, 1, 8, 8, 64, float("nan"), 4, 0, None) == 4
     assert f(A, A, A, A, A + 4, 1, 1, 8, 8, 64, 0.1, 4, 0, None) == 5
+
+
+def test_dropout_rejects_before_touching_the_device():
+    f = fa.lib().fa2_fwd_dropout
+    assert f(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, None) == 1
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 1, 0.1, 1, 0, None) == 3
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 2, 0.1, 1, 0, None) == 4
+    for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 1, p, 1, 0, None) == 4, p
+    assert f(A, A, A, A, A + 4, 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, None) == 5
 
 
 def test_head_dim_256_only_for_16bit_forward():

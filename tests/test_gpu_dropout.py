@@ -1,0 +1,134 @@
+"""Parity of attention with dropout (fa2_fwd_dropout, through the C ABI) with the
+float64 dropout oracle.
+
+The keep mask is integer work decided by the generator alone, so it is checked
+bit-exactly: with V = I (Lk <= d) the output row i is row i of A = P * Z * 256 / t,
+and its zeros must be exactly the dropped or masked pairs.  Values: the bf16
+bars of fa2_fwd scaled by the keep scale 256 / t (every kept probability, and so
+every rounding error carried by O, grows by that factor): max|dO| <= 2e-2 * 256 / t,
+max|dLSE| <= 1e-3 (the LSE is the one without dropout)."""
+import numpy as np
+import pytest
+import torch
+
+import flashattention_forward_fwd_amd as fa
+from flashattention_forward_fwd_amd.inputs import random_qkv
+from oracle import ref
+from tests.parity import TOL, say, widen
+
+pytestmark = pytest.mark.gpu
+
+
+def run_dropout(q, k, v, causal, scale, p, seed, offset):
+    o, lse = fa.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale, dropout=(p, seed, offset))
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def check(name, q, k, v, causal, scale, p, seed, offset):
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    t = ref.dropout_threshold(p)
+    say("case %s: B,H,Lq,Lk,d=%s causal=%d p=%g (t=%d) seed=%#x offset=%d"
+        % (name, (B, H, Lq, Lk, d), causal, p, t, seed, offset))
+    o, lse = run_dropout(q, k, v, causal, scale, p, seed, offset)
+    o_ref, lse_ref = ref.attention_dropout_f64(widen(q), widen(k), widen(v), scale, causal, seed, offset, t)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), name
+    eo = float(np.max(np.abs(o - o_ref)))
+    el = float(np.max(np.abs(lse - lse_ref)))
+    bar = TOL["bf16"]["o"] * 256.0 / t
+    say("  %-40s max|dO|=%.3e (bar %.2e)  max|dLSE|=%.3e" % (name, eo, bar, el))
+    assert eo <= bar and el <= TOL["bf16"]["lse"], name
+
+
+CASES = [
+    # B, H, Lq, Lk, d, causal, p
+    (1, 2, 300, 300, 128, True, 0.1),
+    (2, 3, 200, 333, 64, False, 0.25),
+    (1, 1, 257, 513, 128, False, 0.5),
+    (1, 2, 300, 300, 32, True, 0.2),
+    (1, 1, 300, 400, 256, True, 0.15),
+    (1, 1, 1, 1, 64, False, 0.3),
+    (1, 1, 130, 70, 128, True, 0.9),
+    (2, 2, 129, 1000, 128, False, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_dropout_forward_parity(case):
+    B, H, Lq, Lk, d, causal, p = case
+    q, k, v = random_qkv(B, H, Lq, Lk, d, "bf16", seed=Lq + Lk + d)
+    check("dropout", q, k, v, causal, float(np.float32(1 / np.sqrt(d))), p, 0x5EED0000 + Lq, Lk)
+
+
+def test_dropout_peaky_rows():
+    q, k, v = random_qkv(1, 2, 400, 400, 128, "bf16", seed=77, q_mult=4.0)
+    check("dropout peaky", q, k, v, True, float(np.float32(1 / np.sqrt(128))), 0.2, 12345, 3)
+
+
+@pytest.mark.parametrize("d,Lk,causal", [(128, 128, False), (128, 100, True), (256, 250, False), (64, 64, True),
+                                         (32, 32, False)])
+def test_dropout_mask_exact(d, Lk, causal):
+    """V = I: the nonzero pattern of O[..., :Lk] is the keep mask (and the causal
+    mask), bit for bit, for a seed using both key words and a nonzero offset."""
+    B, H, Lq = 2, 3, 300
+    q, k, _ = random_qkv(B, H, Lq, Lk, d, "bf16", seed=d + Lk)
+    v = torch.zeros(B, H, Lk, d, dtype=torch.bfloat16)
+    v[:, :, torch.arange(Lk), torch.arange(Lk)] = 1.0
+    p, seed, offset = 0.3, 0x0123456789ABCDEF, 0xDEADBEEF
+    t = ref.dropout_threshold(p)
+    say("case mask_exact d=%d Lk=%d causal=%d" % (d, Lk, causal))
+    o, _ = run_dropout(q, k, v, causal, float(np.float32(1 / np.sqrt(d))), p, seed, offset)
+    want = ref.dropout_mask(B, H, Lq, Lk, seed, offset, t)
+    if causal:
+        want &= np.tril(np.ones((Lq, Lk), dtype=bool))
+    got = o[..., :Lk] != 0
+    say("  kept %d of %d, mismatches %d" % (int(want.sum()), want.size, int((got != want).sum())))
+    assert np.array_equal(got, want)
+    assert np.all(o[..., Lk:] == 0)
+
+
+def test_dropout_zero_rate_is_plain_forward():
+    q, k, v = (x.cuda() for x in random_qkv(1, 2, 300, 300, 128, "bf16", seed=5))
+    o1, l1 = fa.forward(q, k, v, causal=True)
+    o2, l2 = fa.forward(q, k, v, causal=True, dropout=(0.0, 99, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_dropout_seed_and_offset_select_the_mask():
+    q, k, v = (x.cuda() for x in random_qkv(1, 2, 200, 200, 64, "bf16", seed=6))
+    a, la = fa.forward(q, k, v, dropout=(0.2, 7, 0))
+    b, _ = fa.forward(q, k, v, dropout=(0.2, 7, 0))
+    c, _ = fa.forward(q, k, v, dropout=(0.2, 7, 1))
+    e, _ = fa.forward(q, k, v, dropout=(0.2, 7 + (1 << 32), 0))
+    plain, lp = fa.forward(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)                     # deterministic
+    assert not torch.equal(a, c) and not torch.equal(a, e)
+    assert torch.equal(la, lp)                   # the LSE ignores dropout
+
+
+def test_dropout_headline_shape_first_head():
+    """B=2, H=32, N=4096, d=128, causal, p=0.1: head (0, 0) (generator counter word
+    b*H + h = 0) against the oracle run on that head alone; every head's LSE
+    against fa2_fwd's."""
+    B, H, L, d = 2, 32, 4096, 128
+    q, k, v = random_qkv(B, H, L, L, d, "bf16", seed=2024)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    p, seed, offset = 0.1, 0xABCDEF, 17
+    t = ref.dropout_threshold(p)
+    say("case dropout headline B=2 H=32 N=4096 d=128 causal p=0.1")
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    o, lse = fa.forward(qc, kc, vc, causal=True, scale=scale, dropout=(p, seed, offset))
+    _, lse_plain = fa.forward(qc, kc, vc, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(lse, lse_plain)
+    o0 = o[0, 0].double().cpu().numpy()
+    o_ref, l_ref = ref.attention_dropout_f64(widen(q[:1, :1]), widen(k[:1, :1]), widen(v[:1, :1]), scale, True,
+                                             seed, offset, t)
+    eo = float(np.max(np.abs(o0 - o_ref[0, 0])))
+    el = float(np.max(np.abs(lse[0, 0].double().cpu().numpy() - l_ref[0, 0])))
+    bar = TOL["bf16"]["o"] * 256.0 / t
+    say("  head (0,0): max|dO|=%.3e (bar %.2e) max|dLSE|=%.3e" % (eo, bar, el))
+    assert eo <= bar and el <= TOL["bf16"]["lse"]
