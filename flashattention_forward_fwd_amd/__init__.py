@@ -10,7 +10,7 @@ and the stream.
 """
 import math
 
-from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_f16, fa2_bwd_window,  # noqa: F401
+from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_dropout, fa2_bwd_f16, fa2_bwd_window,  # noqa: F401
                    fa2_bwd_workspace_bytes,
                    fa2_check_args, fa2_fwd, fa2_fwd_f16, fa2_fwd_f32, fa2_fwd_splitkv, fa2_fwd_window,
                    fa2_fwd_dropout, fa2_merge_partials,
@@ -18,7 +18,7 @@ from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_f16, fa2_bwd_windo
 
 __all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f16", "fa2_fwd_f32", "fa2_fwd_splitkv",
            "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
-           "fa2_fwd_window", "fa2_fwd_dropout", "fa2_bwd", "fa2_bwd_f16", "fa2_bwd_window", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
+           "fa2_fwd_window", "fa2_fwd_dropout", "fa2_bwd", "fa2_bwd_f16", "fa2_bwd_window", "fa2_bwd_dropout", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
            "FA2_MAX_SPLITS"]
 
 
@@ -122,7 +122,7 @@ def merge_partials(o_parts, lse_parts, out=None, lse=None):
 
 
 def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
-             window=None):
+             window=None, dropout=None):
     """Gradients (dq, dk, dv) of attention for the upstream gradient dout (libfa2 ``fa2_bwd``).
 
     q, k, v, o, dout: bfloat16 (or all float16) CUDA tensors (q, o, dout [B, H, Lq, d]; k, v
@@ -130,8 +130,9 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
     the same q, k, v, causal and scale.  Returns bf16 (dq, dk, dv).  The
     workspace is allocated here unless a large enough uint8 device tensor is
     given.  window: (window_left, window_right) of a ``forward(..., window=...)``
-    call runs ``fa2_bwd_window`` (causal must then be False).  Enqueued on the
-    current stream.
+    call runs ``fa2_bwd_window`` (causal must then be False).  dropout: the
+    (p, seed, offset) of a ``forward(..., dropout=...)`` call runs
+    ``fa2_bwd_dropout`` (bf16).  Enqueued on the current stream.
     """
     import torch
 
@@ -162,6 +163,13 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     nbytes = workspace.numel() * workspace.element_size()
+    if dropout is not None:
+        if window is not None or q.dtype != torch.bfloat16:
+            raise ValueError("dropout takes bfloat16 tensors and no window")
+        p_drop, seed, offset = dropout
+        fa2_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), float(p_drop),
+                        int(seed), int(offset), workspace, nbytes, stream)
+        return dq, dk, dv
     if window is not None:
         if causal or q.dtype != torch.bfloat16:
             raise ValueError("window takes bfloat16 tensors and replaces the causal mask (causal=False)")

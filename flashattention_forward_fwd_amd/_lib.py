@@ -42,6 +42,8 @@ SIGNATURES = {
     "fa2_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
     "fa2_bwd_f16": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _Z, _P]),
     "fa2_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "fa2_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _D, _U64, _U32, _P, _Z,
+                             _P]),
 }
 
 _lib = None
@@ -187,6 +189,17 @@ def fa2_fwd_dropout(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, 
                                float(dropout_p), int(seed), int(offset), _ptr(stream))
     if st != FA2_OK:
         raise FA2Error(st, "fa2_fwd_dropout")
+
+
+def fa2_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset,
+                    workspace, workspace_bytes, stream):
+    """libfa2 ``fa2_bwd_dropout`` (gradients of fa2_fwd_dropout).  Raises FA2Error."""
+    st = lib().fa2_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                               _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
+                               float(dropout_p), int(seed), int(offset), _ptr(workspace), int(workspace_bytes),
+                               _ptr(stream))
+    if st != FA2_OK:
+        raise FA2Error(st, "fa2_bwd_dropout")
 
 
 def fa2_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, window_left, window_right,

@@ -402,6 +402,22 @@ int fa2_bwd_f16(const void *q, const void *k, const void *v, const void *o, cons
     return FA2_OK;
 }
 
+int fa2_bwd_dropout(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                    void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                    double dropout_p, uint64_t seed, uint32_t offset, void *workspace,
+                    size_t workspace_bytes_given, void *stream)
+{
+    fa2::BwdParams p;
+    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+                         workspace_bytes_given, &p);
+    if (st != FA2_OK) return st;
+    if ((st = dropout_setup(dropout_p, seed, offset, &p.drop)) != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (fa2::launch_bwd_bf16_dropout(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
 int fa2_bwd_window(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                    void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale,
                    int window_left, int window_right, void *workspace, size_t workspace_bytes_given,

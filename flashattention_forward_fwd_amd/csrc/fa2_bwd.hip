@@ -26,6 +26,14 @@
 // being accumulated across key blocks with atomics, which would make the sum
 // order, and so the rounding, depend on scheduling.
 //
+// With dropout (keep mask Z, keep scale ks = 256 / t, A = P * Z * ks the matrix
+// the forward multiplied V by): dV = A^T dO, dP = (dO V^T) * Z * ks,
+// D_i = sum_j A_ij (dO V^T)_ij = sum_t dO_it O_it as before, dS = P * (dP - D).
+// The dV wavefront draws the mask, accumulates (P * Z)^T dO (ks is applied to dV
+// at the end) and hands P to the dK wavefront with the sign bit set on dropped
+// entries (P >= 0, so the sign carries the mask bit; a dropped 0 is -0), so the
+// generator runs once per (row, key) in that kernel.
+//
 // Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A
 // 32x32 score accumulator puts one key (dK/dV kernel) or one query (dQ kernel)
 // on each lane with 16 entries of the other index, in groups of four; that is
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
 constexpr int kDkdvWaves = 8;
 constexpr int kDkdvThreads = kDkdvWaves * kWave;
 
-template <int D, bool MASKED, typename E>
+template <int D, bool MASKED, typename E, bool DROPOUT>
 __global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dkdv_kernel(BwdParams p)
 {
@@ -340,6 +348,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 // Chunk c (B operand of the products over the tile's rows) holds
                 // rows 16c + 8(e/4) + 4hh + e%4, e = 0..7: entries 8(c%2) + e of half c/2.
                 LDS_AS e8 *pdst = (LDS_AS e8 *)((t & 1) ? sP1 : sP0) + grp * 4 * kWave;
+                DropMask mk;
+                if (DROPOUT) mk = mask_key_lanes(p.drop, t * kRowTile, key, lane, bh);
                 e8 pf[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -357,9 +367,16 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                             pv = hidden ? 0.f : pv;
                         }
                         v8[e] = pv;
+                        if (DROPOUT && !keep(mk, h, i0 + e, p.drop.threshold)) v8[e] = -pv;
                     }
                     pf[c] = __builtin_convertvector(v8, e8);
                     pdst[c * kWave + lane] = pf[c];
+                    if (DROPOUT) {
+                        // dropped (negative) entries -> 0 for this wavefront's product
+                        typedef short s8 __attribute__((ext_vector_type(8)));
+                        const s8 bits = __builtin_bit_cast(s8, pf[c]);
+                        pf[c] = __builtin_bit_cast(e8, __builtin_elementwise_max(bits, s8{}));
+                    }
                 }
                 // dV^T += dO^T P (contraction over the tile's rows).
 #pragma unroll
@@ -394,8 +411,16 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                     const f32x4 d4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 8 + 4 * hh);
                     f32x8 v8;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)   // dS = P (dP - D)
-                        v8[e] = (float)pc[e] * (dp[h][i0 + e] - (e < 4 ? d4a[e] : d4b[e - 4]));
+                    for (int e = 0; e < 8; ++e) {   // dS = P (dP - D)
+                        const float dl = e < 4 ? d4a[e] : d4b[e - 4];
+                        if (DROPOUT) {
+                            const float pr = (float)pc[e];
+                            const float dpz = __builtin_signbit(pr) ? 0.0f : dp[h][i0 + e] * p.drop.keep_scale;
+                            v8[e] = __builtin_fabsf(pr) * (dpz - dl);
+                        } else {
+                            v8[e] = (float)pc[e] * (dp[h][i0 + e] - dl);
+                        }
+                    }
                     dsf[c] = __builtin_convertvector(v8, e8);
                 }
                 // dK^T += Q^T dS (contraction over the tile's rows).
@@ -413,11 +438,11 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     if (key >= p.Lk) return;
     const size_t kv_row = (size_t)bh * p.Lk + key;
     if (is_dk) store_tokens<D, E>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc, p.scale, hh);
-    else       store_tokens<D, E>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc, 1.0f, hh);
+    else       store_tokens<D, E>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc, DROPOUT ? p.drop.keep_scale : 1.0f, hh);
 }
 
 // ---------------------------------------------------------------- 3. dQ
-template <int D, bool MASKED, typename E>
+template <int D, bool MASKED, typename E, bool DROPOUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_bwd_dq_kernel(BwdParams p)
 {
@@ -531,6 +556,8 @@ void fa2_bwd_dq_kernel(BwdParams p)
             }
             // Entry i of tile t is key 64(t0 + j) + 32t + 8(i/4) + 4hh + i%4.
             const bool need_mask = j < plain_lo || j >= n_plain;
+            DropMask mk;
+            if (DROPOUT) mk = mask_query_lanes(p.drop, (t0 + j) * kBc, qrow, lane, bh);
             e8 dsf[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -546,7 +573,10 @@ void fa2_bwd_dq_kernel(BwdParams p)
                         if (MASKED) hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
                         pv = hidden ? 0.f : pv;
                     }
-                    ds8[e] = pv * (dp[t][i] - dlt);
+                    if (DROPOUT)
+                        ds8[e] = pv * ((keep(mk, t, i, p.drop.threshold) ? dp[t][i] * p.drop.keep_scale : 0.0f) - dlt);
+                    else
+                        ds8[e] = pv * (dp[t][i] - dlt);
                 }
                 dsf[c] = __builtin_convertvector(ds8, e8);
             }
@@ -565,7 +595,7 @@ void fa2_bwd_dq_kernel(BwdParams p)
     store_tokens<D, E>(static_cast<uint16_t *>(p.dq) + qoff * D, acc, p.scale, hh);
 }
 
-template <int D, typename E>
+template <int D, typename E, bool DROPOUT = false>
 hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const void *o, const float *lse,
                         hipStream_t stream)
 {
@@ -576,13 +606,15 @@ hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const voi
     BwdParams pk = p;
     pk.n_blocks = (p.Lk + kKeyBlock - 1) / kKeyBlock;
     pk.n_wg = pk.n_blocks * p.B * p.H;
-    if (masked) hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true, E>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
-    else        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false, E>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+    if (masked)
+        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true, E, DROPOUT>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+    else
+        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false, E, DROPOUT>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
     BwdParams pq = p;
     pq.n_blocks = (p.Lq + kBr - 1) / kBr;
     pq.n_wg = pq.n_blocks * p.B * p.H;
-    if (masked) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true, E>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
-    else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false, E>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    if (masked) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true, E, DROPOUT>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false, E, DROPOUT>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
     return hipGetLastError();
 }
 
@@ -603,6 +635,17 @@ hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float 
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
     with_head_dim(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, _Float16>(p, masked, rows, o, lse, stream); });
+    return err;
+}
+
+hipError_t launch_bwd_bf16_dropout(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream)
+{
+    const int64_t rows = (int64_t)p.B * p.H * p.Lq;
+    const bool masked = p.wl >= 0 || p.wr >= 0;
+    hipError_t err = hipSuccess;
+    with_head_dim(d, [&](auto dim) {
+        err = launch_bwd_d<decltype(dim)::value, __bf16, true>(p, masked, rows, o, lse, stream);
+    });
     return err;
 }
 

@@ -16,6 +16,14 @@ namespace fa2 {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Dropout settings of one call.
+struct DropoutParams {
+    uint32_t seed_lo, seed_hi;   // Philox key
+    uint32_t offset;             // fourth counter word
+    uint32_t threshold;          // keep iff byte < threshold, 1..256
+    float keep_scale;            // 256 / threshold
+};
+
 // Philox4x32-10: ten rounds of two 32x32->64-bit products (multipliers
 // 0xD2511F53 and 0xCD9E8D57), the key bumped by the Weyl constants 0x9E3779B9 and
 // 0xBB67AE85 between rounds.  The key is wave-uniform, so its schedule runs on
@@ -70,12 +78,55 @@ __device__ __forceinline__ u32x4_t byte_transpose(u32x4_t w)
     return c;
 }
 
-// Dropout settings of one call.
-struct DropoutParams {
-    uint32_t seed_lo, seed_hi;   // Philox key
-    uint32_t offset;             // fourth counter word
-    uint32_t threshold;          // keep iff byte < threshold, 1..256
-    float keep_scale;            // 256 / threshold
+// Keep bytes of one 64 x 32 score block held as two 32x32 accumulators, for
+// one lane.  Word g of y[t] covers entries 4g .. 4g + 3 of accumulator t (the
+// four consecutive indices of the lane's column), one byte each, least
+// significant first.
+struct DropMask {
+    u32x4_t y[2];
 };
+
+// Entry e (0..15) of accumulator t is kept iff its byte is below the threshold.
+__device__ __forceinline__ bool keep(const DropMask &mk, int t, int e, uint32_t threshold)
+{
+    return ((mk.y[t][e / 4] >> (8 * (e % 4))) & 0xFFu) < threshold;
+}
+
+// One query per lane (the forward and dQ kernels): lane l holds query `qrow`
+// (qrow % 4 == l % 4) and, in accumulator t, keys k0 + 32t + 8(e/4) + 4(l/32)
+// + e%4.  The four keys of one row of four entries form one 4-key block, and the
+// four lanes of a quad hold the four queries of one 4-query block, so each lane
+// of the quad draws one block per accumulator (its own index s as the 4-key
+// group) and the transpose hands every lane the word of its own query.
+__device__ __forceinline__ DropMask mask_query_lanes(const DropoutParams &dp, int k0, int qrow, int lane, int bh)
+{
+    DropMask mk;
+    const int s = lane & 3, hh = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t kblock = (uint32_t)(k0 / 4 + 8 * t + 2 * s + hh);
+        mk.y[t] = quad_transpose(philox4x32_10(kblock, (uint32_t)qrow / 4u, (uint32_t)bh, dp.offset,
+                                               dp.seed_lo, dp.seed_hi), s);
+    }
+    return mk;
+}
+
+// One key per lane (the dK/dV kernel): lane l holds key `key` (key % 4 == l % 4)
+// and, in accumulator t, query rows r0 + 32t + 8(e/4) + 4(l/32) + e%4.  Each
+// lane of a quad draws the block of one 4-row group; its bytes are transposed
+// within the lane (word w byte b -> word b byte w: the 4 rows of key b) and then
+// across the quad, so every lane gets the rows of its own key.
+__device__ __forceinline__ DropMask mask_key_lanes(const DropoutParams &dp, int r0, int key, int lane, int bh)
+{
+    DropMask mk;
+    const int s = lane & 3, hh = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const uint32_t rblock = (uint32_t)(r0 / 4 + 8 * t + 2 * s + hh);
+        mk.y[t] = quad_transpose(byte_transpose(philox4x32_10((uint32_t)key / 4u, rblock, (uint32_t)bh, dp.offset,
+                                                              dp.seed_lo, dp.seed_hi)), s);
+    }
+    return mk;
+}
 
 }  // namespace fa2

@@ -231,30 +231,13 @@ __device__ __forceinline__ float reference_max(float m)
     return (EMPTY_ROWS && m == -INFINITY) ? 0.0f : m;
 }
 
-// Dropout keep bytes of one score tile for this lane: word g of y[t] holds the
-// generator bytes of keys k0 + 32t + 8g + 4hh + 0..3 (byte = key mod 4) of the
-// lane's query.  Those keys form one 4-key block, and the four lanes of a quad
-// (queries 4a .. 4a + 3) share its 4-query block, so lane s of the quad computes
-// the blocks g = s of both t and the quad transpose hands each lane the word of
-// its own query (word = query mod 4; q0 is a multiple of 4).
-struct TileMask {
-    u32x4 y[2];
-};
-
+// Dropout keep bytes of one score tile for this lane (the lane's query qrow is
+// q0 + lane % 32 with q0 a multiple of 32, so qrow % 4 == lane % 4).
 template <bool DROPOUT>
-__device__ __forceinline__ TileMask tile_mask(const DropoutParams &dp, int k0, int qrow, int lane, int bh)
+__device__ __forceinline__ DropMask tile_mask(const DropoutParams &dp, int k0, int qrow, int lane, int bh)
 {
-    TileMask mk;
-    if (DROPOUT) {
-        const int s = lane & 3, hh = lane >> 5;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint32_t kblock = (uint32_t)(k0 / 4 + 8 * t + 2 * s + hh);
-            mk.y[t] = quad_transpose(philox4x32_10(kblock, (uint32_t)qrow / 4u, (uint32_t)bh, dp.offset,
-                                                   dp.seed_lo, dp.seed_hi), s);
-        }
-    }
-    return mk;
+    if (DROPOUT) return mask_query_lanes(dp, k0, qrow, lane, bh);
+    return DropMask{};
 }
 
 // P~ = 2^(S c - m) as bf16 B operands (one per 16-key chunk: slots 0-3 are keys
@@ -263,7 +246,7 @@ __device__ __forceinline__ TileMask tile_mask(const DropoutParams &dp, int k0, i
 // operands (the 1 / keep-rate factor is applied to O at the end).
 template <typename E, bool DROPOUT = false>
 __device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, float m, typename V16<E>::x8 (&pf)[4],
-                                               const TileMask &mk = TileMask{}, uint32_t thr = 256)
+                                               const DropMask &mk = DropMask{}, uint32_t thr = 256)
 {
     float rs = 0.f;
 #pragma unroll
@@ -274,10 +257,7 @@ __device__ __forceinline__ float probabilities(const f32x16 (&s)[2], float c2, f
         for (int e = 0; e < 8; ++e) {
             v8[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i0 + e], c2, -m));
             rs += v8[e];
-            if (DROPOUT) {
-                const uint32_t u = (mk.y[t][2 * (c & 1) + e / 4] >> (8 * (e % 4))) & 0xFFu;
-                v8[e] = u < thr ? v8[e] : 0.0f;
-            }
+            if (DROPOUT) v8[e] = keep(mk, t, i0 + e, thr) ? v8[e] : 0.0f;
         }
         pf[c] = __builtin_convertvector(v8, typename V16<E>::x8);
     }
@@ -327,7 +307,7 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
 {
     if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
     typename V16<E>::x8 pf[4];
-    const TileMask mk = tile_mask<DROPOUT>(dp, (t0 + j) * kBc, qrow, lane, bh);
+    const DropMask mk = tile_mask<DROPOUT>(dp, (t0 + j) * kBc, qrow, lane, bh);
     const float rs = probabilities<E, DROPOUT>(s_cur, c2, reference_max<EMPTY_ROWS>(m), pf, mk, dp.threshold);
     f32x16 s_next[2];
     scores<D, E>(k_next, qf, s_next, k_lane);
@@ -544,7 +524,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         if (j + 1 < n_kv) load_tile_async<D, true>(rV, t0 + j + 1, odd ? sV0 : sV1, wave, loff);
         if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
         e8 pf[4];
-        const TileMask mk = tile_mask<DROPOUT>(p.drop, (t0 + j) * kBc, qrow, lane, bh);
+        const DropMask mk = tile_mask<DROPOUT>(p.drop, (t0 + j) * kBc, qrow, lane, bh);
         lpart += probabilities<E, DROPOUT>(s_cur, c2, reference_max<kEmptyRows>(m), pf, mk, p.drop.threshold);
         accumulate_pv<D, E>((const LDS_AS char *)(odd ? sV1 : sV0), pf, acc_o, v_lane);
         __builtin_amdgcn_s_waitcnt(0);

@@ -141,6 +141,8 @@ hipError_t launch_fwd_bf16_dropout(const FwdParams &p, int d, bool causal, hipSt
 // for the keys p.wl / p.wr leave visible.
 hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
 hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
+// Backward of the dropout forward (bf16): p.drop as given to that forward.
+hipError_t launch_bwd_bf16_dropout(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                         int d, void *o, float *lse, hipStream_t stream);
 }  // namespace fa2

@@ -263,6 +263,22 @@ int fa2_bwd_f16(const void *q, const void *k, const void *v, const void *o, cons
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Backward pass of fa2_fwd_dropout: the gradients of o = (P * Z * 256 / t) V with
+ * the keep mask Z of (dropout_p, seed, offset) -- pass exactly the values given to
+ * the forward that wrote o and lse; the mask is drawn again, not stored.  With
+ * A = P * Z * 256 / t:
+ *     dv = A^T dout,   dP = (dout v^T) * Z * 256 / t,   D = rowsum(dout * o),
+ *     dS = P * (dP - D),   dq = scale dS k,   dk = scale dS^T q
+ * (the derivative of that forward; the reading is described at fa2_fwd_dropout).
+ * Same arguments, precision, workspace and error rules as fa2_bwd; FA2_ERR_ARG
+ * also for dropout_p outside [0, 1).
+ */
+int fa2_bwd_dropout(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                    void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                    double dropout_p, uint64_t seed, uint32_t offset, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
  * Backward pass of fa2_fwd_window: the gradients of attention over the key
  * window (window_left, window_right) of fa2_fwd_window, from its o and lse.
  * Rows that see no key contribute nothing (their o = 0, D = 0, P = 0); keys no

@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
                                          "fa2_fwd_splitkv", "fa2_splitkv_workspace_bytes",
                                          "fa2_splitkv_num_splits", "fa2_merge_partials",
                                          "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd_window",
-                                         "fa2_bwd_window", "fa2_bwd_f16", "fa2_fwd_dropout"])
+                                         "fa2_bwd_window", "fa2_bwd_f16", "fa2_fwd_dropout",
+                                         "fa2_bwd_dropout"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -184,6 +185,12 @@ def test_dropout_rejects_before_touching_the_device():
     for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
         assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 1, p, 1, 0, None) == 4, p
     assert f(A, A, A, A, A + 4, 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, None) == 5
+    g = fa.lib().fa2_bwd_dropout
+    big = 1 << 30
+    assert g(None, *([A] * 8), 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, A, big, None) == 1
+    assert g(*([A] * 9), 1, 1, 8, 8, 256, 0.1, 1, 0.1, 1, 0, A, big, None) == 3
+    assert g(*([A] * 9), 1, 1, 8, 8, 64, 0.1, 1, 1.0, 1, 0, A, big, None) == 4
+    assert g(*([A] * 9), 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, A, 4, None) == 8
 
 
 def test_head_dim_256_only_for_16bit_forward():

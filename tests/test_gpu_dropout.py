@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import flashattention_forward_fwd_amd as fa
-from flashattention_forward_fwd_amd.inputs import random_qkv
+from flashattention_forward_fwd_amd.inputs import random_dout, random_qkv
 from oracle import ref
 from tests.parity import TOL, say, widen
 
@@ -132,3 +132,108 @@ def test_dropout_headline_shape_first_head():
     bar = TOL["bf16"]["o"] * 256.0 / t
     say("  head (0,0): max|dO|=%.3e (bar %.2e) max|dLSE|=%.3e" % (eo, bar, el))
     assert eo <= bar and el <= TOL["bf16"]["lse"]
+
+
+# ------------------------------------------------------------------ backward
+def grad_bar(g_ref, t):
+    """Backward bar with dropout: 2e-2 * max(256 / t, max|G_ref|) -- the bf16 bar of
+    the plain backward with its O(1) floor raised by the keep scale, the factor on
+    every kept probability and on dP."""
+    return 2e-2 * max(256.0 / t, float(np.abs(g_ref).max()))
+
+
+def run_dropout_bwd(q, k, v, do, causal, scale, p, seed, offset):
+    tq, tk, tv, tdo = (x.cuda() for x in (q, k, v, do))
+    o, lse = fa.forward(tq, tk, tv, causal=causal, scale=scale, dropout=(p, seed, offset))
+    grads = fa.backward(tq, tk, tv, o, lse, tdo, causal=causal, scale=scale, dropout=(p, seed, offset))
+    torch.cuda.synchronize()
+    return [g.double().cpu().numpy() for g in grads]
+
+
+def check_bwd(name, q, k, v, do, causal, scale, p, seed, offset):
+    B, H, Lq, d = q.shape
+    Lk = k.shape[2]
+    t = ref.dropout_threshold(p)
+    say("case %s: B,H,Lq,Lk,d=%s causal=%d p=%g (t=%d)" % (name, (B, H, Lq, Lk, d), causal, p, t))
+    got = run_dropout_bwd(q, k, v, do, causal, scale, p, seed, offset)
+    want = ref.attention_dropout_f64(widen(q), widen(k), widen(v), scale, causal, seed, offset, t, dout=widen(do))[2:]
+    for gname, g, w in zip(("dq", "dk", "dv"), got, want):
+        assert np.all(np.isfinite(g)), "%s %s: non-finite" % (name, gname)
+        err = float(np.max(np.abs(g - w)))
+        bar = grad_bar(w, t)
+        say("  %-32s %s max|err|=%.3e (bar %.3e, max|G|=%.3e)" % (name, gname, err, bar, float(np.abs(w).max())))
+        assert err <= bar, "%s %s" % (name, gname)
+
+
+BWD_CASES = [
+    # B, H, Lq, Lk, d, causal, p
+    (1, 2, 300, 300, 128, True, 0.1),
+    (2, 3, 200, 333, 64, False, 0.25),
+    (1, 1, 257, 513, 128, False, 0.5),
+    (1, 2, 300, 300, 32, True, 0.2),
+    (1, 1, 130, 70, 128, True, 0.9),
+    (1, 1, 1, 1, 64, False, 0.3),
+    (2, 2, 129, 1000, 128, False, 0.05),
+    (1, 1, 640, 640, 128, True, 0.3),
+    (1, 1, 333, 129, 64, True, 0.6),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(map(str, c)))
+def test_dropout_backward_parity(case):
+    B, H, Lq, Lk, d, causal, p = case
+    q, k, v = random_qkv(B, H, Lq, Lk, d, "bf16", seed=Lq + 2 * Lk + d)
+    do = random_dout(B, H, Lq, d, "bf16", seed=Lq + 2 * Lk + d)
+    check_bwd("dropout bwd", q, k, v, do, causal, float(np.float32(1 / np.sqrt(d))), p, 0xC0FFEE + Lk, Lq)
+
+
+def test_dropout_backward_zero_rate_is_plain_backward():
+    q, k, v = (x.cuda() for x in random_qkv(1, 2, 300, 300, 128, "bf16", seed=8))
+    do = random_dout(1, 2, 300, 128, "bf16", seed=8).cuda()
+    o, lse = fa.forward(q, k, v, causal=True)
+    g1 = fa.backward(q, k, v, o, lse, do, causal=True)
+    g2 = fa.backward(q, k, v, o, lse, do, causal=True, dropout=(0.0, 5, 5))
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d,Lq,causal", [(128, 128, False), (128, 100, True), (64, 64, False), (32, 32, True)])
+def test_dropout_backward_mask_exact(d, Lq, causal):
+    """dout = I (Lq <= d): dv[j, i] = (256 / t) P[i, j] Z[i, j], so the nonzero
+    pattern of dv[..., :Lq] is the transposed keep mask (and the causal mask) bit
+    for bit -- the mask as the key-per-lane kernel draws it."""
+    B, H, Lk = 2, 3, 300
+    q, k, v = random_qkv(B, H, Lq, Lk, d, "bf16", seed=d + Lq + 1)
+    do = torch.zeros(B, H, Lq, d, dtype=torch.bfloat16)
+    do[:, :, torch.arange(Lq), torch.arange(Lq)] = 1.0
+    p, seed, offset = 0.3, 0xFEDCBA9876543210, 42
+    t = ref.dropout_threshold(p)
+    say("case bwd mask_exact d=%d Lq=%d causal=%d" % (d, Lq, causal))
+    _, _, dv = run_dropout_bwd(q, k, v, do, causal, float(np.float32(1 / np.sqrt(d))), p, seed, offset)
+    want = ref.dropout_mask(B, H, Lq, Lk, seed, offset, t)
+    if causal:
+        want &= np.tril(np.ones((Lq, Lk), dtype=bool))
+    got = np.swapaxes(dv[..., :Lq], -1, -2) != 0
+    say("  kept %d of %d, mismatches %d" % (int(want.sum()), want.size, int((got != want).sum())))
+    assert np.array_equal(got, want)
+
+
+def test_dropout_backward_headline_shape_first_head():
+    """B=2, H=32, N=4096, d=128, causal, p=0.1: the gradients of head (0, 0)
+    against the oracle run on that head alone."""
+    B, H, L, d = 2, 32, 4096, 128
+    q, k, v = random_qkv(B, H, L, L, d, "bf16", seed=2025)
+    do = random_dout(B, H, L, d, "bf16", seed=2025)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    p, seed, offset = 0.1, 0x1234, 99
+    t = ref.dropout_threshold(p)
+    say("case dropout backward headline B=2 H=32 N=4096 d=128 causal p=0.1")
+    got = run_dropout_bwd(q, k, v, do, True, scale, p, seed, offset)
+    want = ref.attention_dropout_f64(widen(q[:1, :1]), widen(k[:1, :1]), widen(v[:1, :1]), scale, True, seed,
+                                     offset, t, dout=widen(do[:1, :1]))[2:]
+    for gname, g, w in zip(("dq", "dk", "dv"), got, want):
+        err = float(np.max(np.abs(g[0, 0] - w[0, 0])))
+        bar = grad_bar(w, t)
+        say("  head (0,0) %s max|err|=%.3e (bar %.3e)" % (gname, err, bar))
+        assert err <= bar, gname
