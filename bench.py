@@ -40,11 +40,13 @@ CONTEXT = {
 
 
 def kernel_source_digest():
-    """sha256 over the HIP sources, to tell whether stored counters are stale."""
+    """sha256 over the sources of the one-pass forward kernel and its launch (the
+    kernel file, the shared headers and the entry points), to tell whether stored
+    counters are stale.  The backward, merge and fp32 sources do not enter it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "flashattention_forward_fwd_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith(".h") or name in ("fa2_fwd_bf16.hip", "fa2_api.hip"):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -145,6 +147,9 @@ def main():
                          "way, rounded to IEEE half")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass fa2_bwd (bf16 workloads) instead of the forward")
+    ap.add_argument("--dropout", type=float, default=None, metavar="P",
+                    help="time the dropout entry point (fa2_fwd_dropout, or fa2_bwd_dropout with --backward) "
+                         "with drop probability P on a bf16 workload; seed and offset fixed")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -183,6 +188,15 @@ def main():
     bwd_info = None
     win_info = None
     flops_override = None
+    drop_info = None
+    if args.dropout is not None:
+        if w.dtype != "bf16" or args.splits is not None or args.window is not None or args.fp16:
+            print("bench.py: --dropout takes a bf16 workload, without --splits, --window or --fp16",
+                  file=sys.stderr)
+            sys.exit(2)
+        drop_args = (float(args.dropout), 0x5EED, 0)
+        drop_info = {"p": float(args.dropout), "seed": 0x5EED, "offset": 0,
+                     "flops_count": "as without dropout (the mask adds no matrix work)"}
     if args.window is not None:
         if w.dtype != "bf16" or args.splits is not None or args.backward:
             print("bench.py: --window takes a bf16 workload, without --splits or --backward",
@@ -206,16 +220,25 @@ def main():
         from flashattention_forward_fwd_amd.inputs import random_dout
         do = random_dout(w.B, w.H, w.Lq, w.d, w.dtype, seed=w.seed)
         ddo = do.cuda()
-        (fa.fa2_fwd_f16 if w.dtype == "fp16" else fa.fa2_fwd)(*(args_common + (stream.cuda_stream,)))
+        if drop_info is not None:
+            fa.fa2_fwd_dropout(*(args_common + drop_args + (stream.cuda_stream,)))
+        else:
+            (fa.fa2_fwd_f16 if w.dtype == "fp16" else fa.fa2_fwd)(*(args_common + (stream.cuda_stream,)))
         gq, gk, gv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
         ws_bytes = fa.fa2_bwd_workspace_bytes(w.B, w.H, w.Lq)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         fn = fa.fa2_bwd_f16 if w.dtype == "fp16" else fa.fa2_bwd
         call = (dq, dk, dv, o, lse, ddo, gq, gk, gv, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal),
                 workspace, ws_bytes, stream.cuda_stream)
+        if drop_info is not None:
+            fn = fa.fa2_bwd_dropout
+            call = call[:16] + drop_args + call[16:]
         bwd_info = {"timed_call": "fa2_bwd = prep + dK/dV + dQ kernels", "workspace_bytes": ws_bytes,
                     "flops_count": "2.5x forward (S, dP, dV, dK, dQ); the dQ pass recomputes S and dP, "
                                    "so the device executes 3.5x"}
+    elif drop_info is not None:
+        fn = fa.fa2_fwd_dropout
+        call = args_common + drop_args + (stream.cuda_stream,)
     elif args.splits is None:
         fn = {"bf16": fa.fa2_fwd, "fp16": fa.fa2_fwd_f16, "fp32": fa.fa2_fwd_f32}[w.dtype]
         call = args_common + (stream.cuda_stream,)
@@ -257,7 +280,7 @@ def main():
     # dense fp16 MFMA has the same published peak as bf16 on MI355X
     peak = PEAK_FP32_MFMA_TFLOPS if w.dtype == "fp32" else PEAK_BF16_TFLOPS
     traffic = (stored_traffic(w.name) if split_info is None and bwd_info is None and win_info is None
-               and not args.fp16 else None)
+               and drop_info is None and not args.fp16 else None)
     algo_bytes = (4 if w.dtype == "fp32" else 2) * w.B * w.H * (2 * w.Lq + 2 * w.Lk) * w.d + 4 * w.B * w.H * w.Lq
     if bwd_info:
         # reads q, k, v, o, dout, lse; writes dq, dk, dv
@@ -292,11 +315,14 @@ def main():
     if win_info is not None:
         out["config"]["window"] = win_info
         out["metric"] = "attention fwd TFLOPS (4·d per visible query-key pair) bf16, sliding window"
+    if drop_info is not None:
+        out["config"]["dropout"] = drop_info
+        out["metric"] = out["metric"] + ", dropout"
     if bwd_info is not None:
         out["config"]["backward"] = bwd_info
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and drop_info is None:
             out["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do)
-    elif not args.no_cpu_baseline and win_info is None:
+    elif not args.no_cpu_baseline and win_info is None and drop_info is None:
         n = args.cpu_rows_per_head if args.cpu_rows_per_head > 0 else w.Lq
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, min(n, w.Lq))
     print(json.dumps(out), flush=True)

@@ -32,7 +32,9 @@
 // The dV wavefront draws the mask, accumulates (P * Z)^T dO (ks is applied to dV
 // at the end) and hands P to the dK wavefront with the sign bit set on dropped
 // entries (P >= 0, so the sign carries the mask bit; a dropped 0 is -0), so the
-// generator runs once per (row, key) in that kernel.
+// generator runs once per (row, key) in that kernel.  The prep kernel stores
+// D / ks, so dS / ks = P * (dO V^T * Z - D / ks) needs no product with ks per
+// entry; dK and dQ take the factor ks with the scale at the end.
 //
 // Every product runs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A
 // 32x32 score accumulator puts one key (dK/dV kernel) or one query (dQ kernel)
@@ -182,7 +184,7 @@ __device__ __forceinline__ void store_tokens(uint16_t *dst_row, const f32x16 (&a
 // D_i = sum_t dO_it O_it (fp32) and lse2_i = lse_i * log2(e); D/8 threads per row.
 template <int D, typename E>
 __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, const uint16_t *dout, const float *lse,
-                                                           float *lse2, float *delta, int64_t rows)
+                                                           float *lse2, float *delta, int64_t rows, float dmul)
 {
     constexpr int kTpr = D / 8;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
     for (int off = kTpr / 2; off > 0; off >>= 1)
         acc += __shfl_xor(acc, off, kTpr);
     if (row < rows && part == 0) {
-        delta[row] = acc;
+        delta[row] = acc * dmul;
         lse2[row] = lse[row] * kLog2e;
     }
 }
@@ -413,10 +415,9 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {   // dS = P (dP - D)
                         const float dl = e < 4 ? d4a[e] : d4b[e - 4];
-                        if (DROPOUT) {
+                        if (DROPOUT) {   // dS / ks, dl = D / ks
                             const float pr = (float)pc[e];
-                            const float dpz = __builtin_signbit(pr) ? 0.0f : dp[h][i0 + e] * p.drop.keep_scale;
-                            v8[e] = __builtin_fabsf(pr) * (dpz - dl);
+                            v8[e] = __builtin_fabsf(pr) * (__builtin_signbit(pr) ? -dl : dp[h][i0 + e] - dl);
                         } else {
                             v8[e] = (float)pc[e] * (dp[h][i0 + e] - dl);
                         }
@@ -437,7 +438,9 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 
     if (key >= p.Lk) return;
     const size_t kv_row = (size_t)bh * p.Lk + key;
-    if (is_dk) store_tokens<D, E>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc, p.scale, hh);
+    if (is_dk)
+        store_tokens<D, E>(static_cast<uint16_t *>(p.dk) + kv_row * D, acc,
+                           DROPOUT ? p.scale * p.drop.keep_scale : p.scale, hh);
     else       store_tokens<D, E>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc, DROPOUT ? p.drop.keep_scale : 1.0f, hh);
 }
 
@@ -541,58 +544,109 @@ void fa2_bwd_dq_kernel(BwdParams p)
         const LDS_AS char *kbuf = (const LDS_AS char *)(odd ? sK1 : sK0);
         const LDS_AS char *vbuf = (const LDS_AS char *)(odd ? sV1 : sV0);
         if (j < n_wave) {
-            // S^T = K Q^T and dP^T = V dO^T: (keys x this wavefront's queries).
-            f32x16 s[2], dp[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                s[t] = f32x16{};
-                dp[t] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < kDc; ++c)
-                    s[t] = mfma_32x32x16(read_rows_op<D, E>(kbuf, 32 * t + l32, c, hh), qf[c], s[t]);
-#pragma unroll
-                for (int c = 0; c < kDc; ++c)
-                    dp[t] = mfma_32x32x16(read_rows_op<D, E>(vbuf, 32 * t + l32, c, hh), of[c], dp[t]);
-            }
-            // Entry i of tile t is key 64(t0 + j) + 32t + 8(i/4) + 4hh + i%4.
+            // Entry i of score tile t is key 64(t0 + j) + 32t + 8(i/4) + 4hh + i%4.
             const bool need_mask = j < plain_lo || j >= n_plain;
-            DropMask mk;
-            if (DROPOUT) mk = mask_query_lanes(p.drop, (t0 + j) * kBc, qrow, lane, bh);
-            e8 dsf[4];
+            if constexpr (DROPOUT) {
+                // S^T = K Q^T and dP^T = V dO^T for the 32 keys of half t (keys x
+                // this wavefront's queries).
+                auto products = [&](int t, f32x16 &s_t, f32x16 &dp_t) {
+                    s_t = f32x16{};
+                    dp_t = f32x16{};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int t = c >> 1, i0 = 8 * (c & 1);
-                f32x8 ds8;
+                    for (int c = 0; c < kDc; ++c)
+                        s_t = mfma_32x32x16(read_rows_op<D, E>(kbuf, 32 * t + l32, c, hh), qf[c], s_t);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int i = i0 + e;
-                    float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -lse2));
-                    if (need_mask) {
-                        const int kk = (t0 + j) * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
-                        bool hidden = kk >= p.Lk;
-                        if (MASKED) hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
-                        pv = hidden ? 0.f : pv;
+                    for (int c = 0; c < kDc; ++c)
+                        dp_t = mfma_32x32x16(read_rows_op<D, E>(vbuf, 32 * t + l32, c, hh), of[c], dp_t);
+                };
+                // dS / ks of half t (dlt = D / ks, keep bytes y of that half) as the B
+                // operands of key chunks 2t, 2t + 1.
+                auto dscores = [&](int t, const f32x16 &s_t, const f32x16 &dp_t, const u32x4 &y, e8 *dsf) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        f32x8 ds8;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int i = 8 * h + e;
+                            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_t[i], c2, -lse2));
+                            if (need_mask) {
+                                const int kk = (t0 + j) * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
+                                bool hidden = kk >= p.Lk;
+                                if (MASKED)
+                                    hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
+                                pv = hidden ? 0.f : pv;
+                            }
+                            const bool kept = ((y[i / 4] >> (8 * (i % 4))) & 0xFFu) < p.drop.threshold;
+                            ds8[e] = pv * (kept ? dp_t[i] - dlt : -dlt);
+                        }
+                        dsf[h] = __builtin_convertvector(ds8, e8);
                     }
-                    if (DROPOUT)
-                        ds8[e] = pv * ((keep(mk, t, i, p.drop.threshold) ? dp[t][i] * p.drop.keep_scale : 0.0f) - dlt);
-                    else
-                        ds8[e] = pv * (dp[t][i] - dlt);
+                };
+                // One 32-key half at a time (products, keep bytes, dS, dQ update):
+                // the generator's registers and one half's accumulators fit beside
+                // Q, dO and dQ in the register budget of two wavefronts per SIMD.
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const u32x4 y = mask_query_lanes_one(p.drop, (t0 + j) * kBc, t, qrow, lane, bh);
+                    f32x16 s_t, dp_t;
+                    products(t, s_t, dp_t);
+                    e8 dsf[2];
+                    dscores(t, s_t, dp_t, y, dsf);
+                    // dQ^T += K^T dS^T over the half's keys.
+#pragma unroll
+                    for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, dt, 2 * t + h, lane), dsf[h], acc[dt]);
                 }
-                dsf[c] = __builtin_convertvector(ds8, e8);
+            } else {
+                // S^T = K Q^T and dP^T = V dO^T: (keys x this wavefront's queries).
+                f32x16 s[2], dp[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    s[t] = f32x16{};
+                    dp[t] = f32x16{};
+#pragma unroll
+                    for (int c = 0; c < kDc; ++c)
+                        s[t] = mfma_32x32x16(read_rows_op<D, E>(kbuf, 32 * t + l32, c, hh), qf[c], s[t]);
+#pragma unroll
+                    for (int c = 0; c < kDc; ++c)
+                        dp[t] = mfma_32x32x16(read_rows_op<D, E>(vbuf, 32 * t + l32, c, hh), of[c], dp[t]);
+                }
+                e8 dsf[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int t = c >> 1, i0 = 8 * (c & 1);
+                    f32x8 ds8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = i0 + e;
+                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -lse2));
+                        if (need_mask) {
+                            const int kk = (t0 + j) * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
+                            bool hidden = kk >= p.Lk;
+                            if (MASKED) hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
+                            pv = hidden ? 0.f : pv;
+                        }
+                        ds8[e] = pv * (dp[t][i] - dlt);
+                    }
+                    dsf[c] = __builtin_convertvector(ds8, e8);
+                }
+                // dQ^T += K^T dS^T (contraction over the tile's keys).
+#pragma unroll
+                for (int dt = 0; dt < kDt; ++dt)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, dt, c, lane), dsf[c], acc[dt]);
             }
-            // dQ^T += K^T dS^T (contraction over the tile's keys).
-#pragma unroll
-            for (int dt = 0; dt < kDt; ++dt)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, dt, c, lane), dsf[c], acc[dt]);
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
     if (!row_ok) return;
-    store_tokens<D, E>(static_cast<uint16_t *>(p.dq) + qoff * D, acc, p.scale, hh);
+    store_tokens<D, E>(static_cast<uint16_t *>(p.dq) + qoff * D, acc, DROPOUT ? p.scale * p.drop.keep_scale : p.scale,
+                       hh);
 }
 
 template <int D, typename E, bool DROPOUT = false>
@@ -602,7 +656,8 @@ hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const voi
     const int64_t threads = rows * (D / 8);
     hipLaunchKernelGGL((fa2_bwd_prep_kernel<D, E>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(p.dout), lse,
-                       const_cast<float *>(p.lse2), const_cast<float *>(p.delta), rows);
+                       const_cast<float *>(p.lse2), const_cast<float *>(p.delta), rows,
+                       DROPOUT ? 1.0f / p.drop.keep_scale : 1.0f);
     BwdParams pk = p;
     pk.n_blocks = (p.Lk + kKeyBlock - 1) / kKeyBlock;
     pk.n_wg = pk.n_blocks * p.B * p.H;

@@ -27,44 +27,61 @@ struct DropoutParams {
 // Philox4x32-10: ten rounds of two 32x32->64-bit products (multipliers
 // 0xD2511F53 and 0xCD9E8D57), the key bumped by the Weyl constants 0x9E3779B9 and
 // 0xBB67AE85 between rounds.  The key is wave-uniform, so its schedule runs on
-// the scalar unit.
+// the scalar unit.  Each product is one v_mad_u64_u32 (both halves at once), each
+// three-way XOR one v_bitop3_b32 (truth table 0x96).
 __device__ __forceinline__ u32x4_t philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                  uint32_t k0, uint32_t k1)
 {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
-        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
-        c0 = hi1 ^ c1 ^ k0;
-        c1 = lo1;
-        c2 = hi0 ^ c3 ^ k1;
-        c3 = lo0;
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+        c1 = (uint32_t)p1;
+        c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
+        c3 = (uint32_t)p0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
     return u32x4_t{c0, c1, c2, c3};
 }
 
-// x[s] from a 4-element vector with a lane-dependent index s.
-__device__ __forceinline__ uint32_t pick4(u32x4_t x, int s)
+// x from lane (this lane XOR 1) / (this lane XOR 2) of the quad (DPP quad_perm
+// [1,0,3,2] and [2,3,0,1]).
+__device__ __forceinline__ uint32_t from_lane_xor1(uint32_t x)
 {
-    const uint32_t a = (s & 1) ? x[1] : x[0];
-    const uint32_t b = (s & 1) ? x[3] : x[2];
-    return (s & 2) ? b : a;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t from_lane_xor2(uint32_t x)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
 }
 
 // Transpose across each group of four consecutive lanes: lane s of the group
-// holds x = X[s][0..3]; afterwards lane v holds y[u] = X[u][v].  Lane s offers
-// X[s][s ^ k] to the lane s ^ k (DPP quad permutation "xor k").
+// holds x = X[s][0..3]; afterwards lane v holds y[u] = X[u][v].  Two butterfly
+// stages: lanes s and s ^ 1 swap the words whose index differs from s in bit 0,
+// then lanes s and s ^ 2 the words whose index differs from s in bit 1
+// (afterwards word w of lane s holds X[s ^ e][w ^ e] with e = s ^ w, = X[w][s]).
 __device__ __forceinline__ u32x4_t quad_transpose(u32x4_t x, int s)
 {
-    const uint32_t e0 = pick4(x, s);
-    const uint32_t e1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pick4(x, s ^ 1), 0xB1, 0xF, 0xF, false);
-    const uint32_t e2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pick4(x, s ^ 2), 0x4E, 0xF, 0xF, false);
-    const uint32_t e3 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pick4(x, s ^ 3), 0x1B, 0xF, 0xF, false);
-    // now e_k = X[s ^ k][s]; y[u] = e_{u ^ s}
-    const u32x4_t e = {e0, e1, e2, e3};
-    return u32x4_t{pick4(e, s), pick4(e, 1 ^ s), pick4(e, 2 ^ s), pick4(e, 3 ^ s)};
+    const bool b0 = s & 1, b1 = (s >> 1) & 1;
+    {
+        const uint32_t r01 = from_lane_xor1(b0 ? x[0] : x[1]);
+        const uint32_t r23 = from_lane_xor1(b0 ? x[2] : x[3]);
+        x[0] = b0 ? r01 : x[0];
+        x[1] = b0 ? x[1] : r01;
+        x[2] = b0 ? r23 : x[2];
+        x[3] = b0 ? x[3] : r23;
+    }
+    {
+        const uint32_t r02 = from_lane_xor2(b1 ? x[0] : x[2]);
+        const uint32_t r13 = from_lane_xor2(b1 ? x[1] : x[3]);
+        x[0] = b1 ? r02 : x[0];
+        x[2] = b1 ? x[2] : r02;
+        x[1] = b1 ? r13 : x[1];
+        x[3] = b1 ? x[3] : r13;
+    }
+    return x;
 }
 
 // Byte transpose within a lane: c[b] byte w = w_in[w] byte b.
@@ -98,16 +115,20 @@ __device__ __forceinline__ bool keep(const DropMask &mk, int t, int e, uint32_t 
 // four lanes of a quad hold the four queries of one 4-query block, so each lane
 // of the quad draws one block per accumulator (its own index s as the 4-key
 // group) and the transpose hands every lane the word of its own query.
+__device__ __forceinline__ u32x4_t mask_query_lanes_one(const DropoutParams &dp, int k0, int t, int qrow, int lane,
+                                                        int bh)
+{
+    const int s = lane & 3, hh = lane >> 5;
+    const uint32_t kblock = (uint32_t)(k0 / 4 + 8 * t + 2 * s + hh);
+    return quad_transpose(philox4x32_10(kblock, (uint32_t)qrow / 4u, (uint32_t)bh, dp.offset, dp.seed_lo, dp.seed_hi),
+                          s);
+}
 __device__ __forceinline__ DropMask mask_query_lanes(const DropoutParams &dp, int k0, int qrow, int lane, int bh)
 {
     DropMask mk;
-    const int s = lane & 3, hh = lane >> 5;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const uint32_t kblock = (uint32_t)(k0 / 4 + 8 * t + 2 * s + hh);
-        mk.y[t] = quad_transpose(philox4x32_10(kblock, (uint32_t)qrow / 4u, (uint32_t)bh, dp.offset,
-                                               dp.seed_lo, dp.seed_hi), s);
-    }
+    for (int t = 0; t < 2; ++t)
+        mk.y[t] = mask_query_lanes_one(dp, k0, t, qrow, lane, bh);
     return mk;
 }
 
