@@ -70,17 +70,17 @@ bool product_fits(int64_t a, int64_t b, int64_t c, int64_t d)
     return a <= lim / d;
 }
 
-// Head dimensions of the 16-bit forward kernels (and the merge), and of the
-// fp32 forward and the backward kernels.
-bool head_dim_ok(int d, bool with_256) { return d == 32 || d == 64 || d == 128 || (with_256 && d == 256); }
+// Head dimensions of the fp32 forward and the backward kernels (32, 64, 128),
+// and of the 16-bit forward kernels and the merge (also 96 and 256).
+bool head_dim_ok(int d, bool fwd16) { return d == 32 || d == 64 || d == 128 || (fwd16 && (d == 96 || d == 256)); }
 
 int prepare(const void *q, const void *k, const void *v, const void *o, const float *lse,
             int B, int H, int Lq, int Lk, int d, float scale, int causal, int elem_bytes,
-            fa2::FwdParams *out, bool with_256 = false)
+            fa2::FwdParams *out, bool fwd16 = false)
 {
     if (!q || !k || !v || !o || !lse) return FA2_ERR_NULL;
     if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0) return FA2_ERR_DIM;
-    if (!head_dim_ok(d, with_256)) return FA2_ERR_UNSUPPORTED_D;
+    if (!head_dim_ok(d, fwd16)) return FA2_ERR_UNSUPPORTED_D;
     if (causal != 0 && causal != 1) return FA2_ERR_ARG;
     if (!(scale > 0.f) || !isfinite(scale)) return FA2_ERR_ARG;
     if (elem_bytes != 2 && elem_bytes != 4) return FA2_ERR_ARG;
@@ -441,7 +441,7 @@ const char *fa2_status_string(int status)
     case FA2_OK: return "ok";
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
     case FA2_ERR_DIM: return "B, H, Lq, Lk must be positive and the sizes must fit (one head's K below 2 GiB)";
-    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128 (or 256 for the 16-bit forward)";
+    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128 (or 96 or 256 for the 16-bit forward)";
     case FA2_ERR_ARG: return "causal must be 0 or 1 and scale finite and positive";
     case FA2_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";

@@ -67,17 +67,24 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(f16x8 a, f16x8 b, f32x16 c)
 
 #define LDS_AS __attribute__((address_space(3)))
 
+// d = 96: a row is 192 bytes in HBM but takes a d = 128 row (256 bytes) in LDS,
+// so the 1 KiB transfers, the swizzles and the transposing reads of d = 128
+// apply unchanged; the four chunks past column 95 are never loaded or read.
 template <int D> struct Tile {
-    static constexpr int kRowBytes = 2 * D;                  // one K or V row, bf16
-    static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per row
+    static constexpr int kLdsD = D == 96 ? 128 : D;          // row length in LDS
+    static constexpr int kRowBytes = 2 * kLdsD;              // one K or V row in LDS, 16-bit
+    static constexpr int kGRowBytes = 2 * D;                 // one K or V row in HBM
+    static constexpr int kChunks = kRowBytes / 16;           // 16-byte chunks per LDS row
+    static constexpr int kGChunks = kGRowBytes / 16;         // ... that hold data
     static constexpr int kRowsPerXfer = 1024 / kRowBytes;    // rows per 1 KiB wave transfer
     static constexpr int kXfersPerWave = kBc * kRowBytes / 1024 / kWaves;
-    static constexpr int kBytes = kBc * kRowBytes;
+    static constexpr int kBytes = kBc * kRowBytes;           // one tile in LDS
+    static constexpr int kGBytes = kBc * kGRowBytes;         // one tile in HBM
     // K swizzle repeats every kKPeriod transfers (see swz_k), V swizzle every
     // kVPeriod (d = 256: a transfer holds two rows, the V swizzle spans four).
-    static constexpr int kKPeriod = D == 256 ? 8 : D == 128 ? 4 : D == 64 ? 2 : 1;
-    static constexpr int kVPeriod = D == 256 ? 2 : 1;
-    static constexpr int kElems = kBc * D;                   // elements per tile
+    static constexpr int kKPeriod = kLdsD == 256 ? 8 : kLdsD == 128 ? 4 : kLdsD == 64 ? 2 : 1;
+    static constexpr int kVPeriod = kLdsD == 256 ? 2 : 1;
+    static constexpr int kElems = kBc * kLdsD;               // elements per LDS tile
     static_assert(kXfersPerWave * kWaves * 1024 == kBc * kRowBytes, "tile must split into 1 KiB transfers");
     static_assert(kXfersPerWave % kKPeriod == 0 && kXfersPerWave % kVPeriod == 0,
                   "a wave's transfers must start at a swizzle period");
@@ -90,7 +97,7 @@ template <int D> struct Tile {
     // two lines, the swizzle moves the chunk within the row's first 16).
     static __device__ __forceinline__ int swz_k(int r)
     {
-        return D >= 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+        return kLdsD >= 128 ? (r & 15) : kLdsD == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
     }
     // V: the transposing read takes 64 consecutive bytes (4 chunks) from each of
     // 4 consecutive rows; moving each row's 4-chunk group to a different
@@ -98,7 +105,7 @@ template <int D> struct Tile {
     // are one 256-byte line already).
     static __device__ __forceinline__ int swz_v(int r)
     {
-        return D >= 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
+        return kLdsD >= 128 ? 4 * (r & 3) : kLdsD == 64 ? 4 * ((r >> 1) & 1) : 0;
     }
 };
 
@@ -106,13 +113,17 @@ template <int D> struct Tile {
 constexpr int kRawBufferFlags = 0x00020000;
 
 // Per-lane byte offsets of the tile loads.  Transfer x of wavefront w moves
-// 1 KiB block b = w * kXfersPerWave + x of the tile; lane l lands at byte 16 l
-// of the block, i.e. row b * kRowsPerXfer + l / kChunks, physical chunk
-// l % kChunks, and reads that row's logical chunk.  The K swizzle depends on
-// b % kKPeriod, the V swizzle on b % kVPeriod.
+// 1 KiB block b = w * kXfersPerWave + x of the LDS tile; lane l lands at byte
+// 16 l of the block, i.e. row b * kRowsPerXfer + l / kChunks, physical chunk
+// l % kChunks, and reads that row's logical chunk from HBM (offsets from the
+// first row of its swizzle period).  The K swizzle depends on b % kKPeriod, the
+// V swizzle on b % kVPeriod.  d = 96: a lane whose logical chunk lies past
+// column 95 loads nothing (k_on / v_on false).
 template <int D> struct LoadOffsets {
     int k[Tile<D>::kKPeriod];
     int v[Tile<D>::kVPeriod];
+    bool k_on[Tile<D>::kKPeriod];
+    bool v_on[Tile<D>::kVPeriod];
 };
 
 template <int D>
@@ -124,12 +135,16 @@ __device__ __forceinline__ LoadOffsets<D> load_offsets(int lane)
 #pragma unroll
     for (int b = 0; b < T::kKPeriod; ++b) {
         const int row = b * T::kRowsPerXfer + lane / T::kChunks;
-        o.k[b] = row * T::kRowBytes + 16 * (phys ^ T::swz_k(row));
+        const int logical = phys ^ T::swz_k(row);
+        o.k[b] = row * T::kGRowBytes + 16 * logical;
+        o.k_on[b] = T::kGChunks == T::kChunks || logical < T::kGChunks;
     }
 #pragma unroll
     for (int b = 0; b < T::kVPeriod; ++b) {
         const int row = b * T::kRowsPerXfer + lane / T::kChunks;
-        o.v[b] = row * T::kRowBytes + 16 * (phys ^ T::swz_v(row));
+        const int logical = phys ^ T::swz_v(row);
+        o.v[b] = row * T::kGRowBytes + 16 * logical;
+        o.v_on[b] = T::kGChunks == T::kChunks || logical < T::kGChunks;
     }
     return o;
 }
@@ -146,8 +161,10 @@ __device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t src, int 
     for (int x = 0; x < T::kXfersPerWave; ++x) {
         const int b = wave * T::kXfersPerWave + x;
         const int voff = IS_V ? off.v[x % T::kVPeriod] : off.k[x % T::kKPeriod];
-        const int soff = tile * T::kBytes + (IS_V ? b - b % T::kVPeriod : b - b % T::kKPeriod) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void *)(dst + b * 512), 16, voff, soff, 0, 0);
+        const bool on = IS_V ? off.v_on[x % T::kVPeriod] : off.k_on[x % T::kKPeriod];
+        const int row0 = (IS_V ? b - b % T::kVPeriod : b - b % T::kKPeriod) * T::kRowsPerXfer;
+        const int soff = tile * T::kGBytes + row0 * T::kGRowBytes;
+        if (on) __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void *)(dst + b * 512), 16, voff, soff, 0, 0);
     }
 }
 
@@ -407,9 +424,9 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     const uint16_t *Q = static_cast<const uint16_t *>(p.q) + (size_t)bh * p.Lq * D;
     const size_t kv_off = (size_t)bh * p.Lk * D;
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const uint16_t *>(p.k) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+        (void *)(static_cast<const uint16_t *>(p.k) + kv_off), 0, p.Lk * T::kGRowBytes, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const uint16_t *>(p.v) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+        (void *)(static_cast<const uint16_t *>(p.v) + kv_off), 0, p.Lk * T::kGRowBytes, kRawBufferFlags);
     const LoadOffsets<D> loff = load_offsets<D>(lane);
 
     const int q0 = qt * kBr + wave * kRowsPerWave;    // first row of this wavefront

@@ -57,9 +57,10 @@ def test_argument_checks(elem):
     assert st(q=0) == 1 and st(lse=0) == 1 and st(v=0) == 1
     assert st(B=0) == 2 and st(H=-1) == 2 and st(Lq=0) == 2 and st(Lk=0) == 2
     assert st(B=1 << 30, H=1 << 30) == 2
-    for d in (0, 16, 96, 512, 127):
+    for d in (0, 16, 80, 112, 512, 127):
         assert st(d=d) == 3
-    assert st(d=256) == (0 if elem == 2 else 3)      # d = 256: 16-bit forward only
+    assert st(d=256) == (0 if elem == 2 else 3)      # d = 96, 256: 16-bit forward only
+    assert st(d=96) == (0 if elem == 2 else 3)
     assert st(causal=2) == 4 and st(causal=-1) == 4
     assert st(scale=0.0) == 4 and st(scale=-1.0) == 4
     assert st(scale=float("inf")) == 4 and st(scale=float("nan")) == 4
@@ -79,7 +80,7 @@ def test_entry_points_reject_before_touching_the_device():
 
 def test_binding_raises_on_error_status():
     with pytest.raises(fa.FA2Error) as e:
-        fa.fa2_fwd(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 0, None)
+        fa.fa2_fwd(A, A, A, A, A, 1, 1, 8, 8, 80, 0.1, 0, None)
     assert e.value.status == 3
 
 
@@ -96,7 +97,7 @@ def test_splitkv_rejects_before_touching_the_device():
     f = L.fa2_fwd_splitkv
     big = 1 << 30
     assert f(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, 1, A, big, None) == 1
-    assert f(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 0, 1, A, big, None) == 3
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 80, 0.1, 0, 1, A, big, None) == 3
     assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, -1, A, big, None) == 4
     assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, fa.FA2_MAX_SPLITS + 1, A, big, None) == 4
     assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, 2, None, big, None) == 8
@@ -109,7 +110,8 @@ def test_splitkv_workspace_bytes():
         rows = B * H * Lq
         o_bytes = -(-S * rows * d * 4 // 256) * 256
         assert fa.fa2_splitkv_workspace_bytes(B, H, Lq, 500, d, 0, S) == o_bytes + S * rows * 4
-    assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 96, 0, 2) == 0
+    assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 80, 0, 2) == 0
+    assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 96, 0, 2) > 0
     assert fa.fa2_splitkv_workspace_bytes(0, 1, 8, 8, 64, 0, 2) == 0
     assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 64, 0, fa.FA2_MAX_SPLITS + 1) == 0
 
@@ -129,7 +131,7 @@ def test_merge_rejects_before_touching_the_device():
     assert f(A, A, 0, 10, 64, A, A, None) == 4
     assert f(A, A, fa.FA2_MAX_SPLITS + 1, 10, 64, A, A, None) == 4
     assert f(A, A, 2, 0, 64, A, A, None) == 2
-    assert f(A, A, 2, 10, 96, A, A, None) == 3
+    assert f(A, A, 2, 10, 80, A, A, None) == 3
     assert f(A, A + 4, 2, 10, 64, A, A, None) == 5
 
 
@@ -171,7 +173,7 @@ def test_backward_refuses_host_tensors():
 def test_window_rejects_before_touching_the_device():
     f = fa.lib().fa2_fwd_window
     assert f(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 4, 0, None) == 1
-    assert f(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 4, 0, None) == 3
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 80, 0.1, 4, 0, None) == 3
     assert f(A, A, A, A, A, 1, 1, 0, 8, 64, 0.1, 4, 0, None) == 2
     assert f(A, A, A, A, A, 1, 1, 8, 8, 64, float("nan"), 4, 0, None) == 4
     assert f(A, A, A, A, A + 4, 1, 1, 8, 8, 64, 0.1, 4, 0, None) == 5
@@ -180,7 +182,7 @@ def test_window_rejects_before_touching_the_device():
 def test_dropout_rejects_before_touching_the_device():
     f = fa.lib().fa2_fwd_dropout
     assert f(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, None) == 1
-    assert f(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 1, 0.1, 1, 0, None) == 3
+    assert f(A, A, A, A, A, 1, 1, 8, 8, 80, 0.1, 1, 0.1, 1, 0, None) == 3
     assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 2, 0.1, 1, 0, None) == 4
     for p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
         assert f(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 1, p, 1, 0, None) == 4, p
@@ -198,6 +200,7 @@ def test_head_dim_256_only_for_16bit_forward():
     big = 1 << 30
     args = [A] * 9
     assert L.fa2_bwd(*args, 1, 1, 8, 8, 256, 0.1, 0, A, big, None) == 3
+    assert L.fa2_fwd_f32(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 0, None) == 3
     assert L.fa2_fwd_f32(A, A, A, A, A, 1, 1, 8, 8, 256, 0.1, 0, None) == 3
     assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 256, 0, 2) > 0
     assert fa.lib().fa2_merge_partials(A, A, 2, 10, 256, A, A + 4, None) == 5

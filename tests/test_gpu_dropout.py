@@ -48,6 +48,7 @@ CASES = [
     (1, 1, 257, 513, 128, False, 0.5),
     (1, 2, 300, 300, 32, True, 0.2),
     (1, 1, 300, 400, 256, True, 0.15),
+    (1, 2, 300, 400, 96, False, 0.2),
     (1, 1, 1, 1, 64, False, 0.3),
     (1, 1, 130, 70, 128, True, 0.9),
     (2, 2, 129, 1000, 128, False, 0.05),
@@ -67,7 +68,7 @@ def test_dropout_peaky_rows():
 
 
 @pytest.mark.parametrize("d,Lk,causal", [(128, 128, False), (128, 100, True), (256, 250, False), (64, 64, True),
-                                         (32, 32, False)])
+                                         (32, 32, False), (96, 96, True)])
 def test_dropout_mask_exact(d, Lk, causal):
     """V = I: the nonzero pattern of O[..., :Lk] is the keep mask (and the causal
     mask), bit for bit, for a seed using both key words and a nonzero offset."""

@@ -37,7 +37,8 @@ def fwd_check(name, q, k, v, causal, scale, rows=None):
 
 
 SHAPES = [(1, 1, 1, 1, 64), (1, 2, 129, 129, 64), (2, 1, 257, 255, 128), (1, 1, 300, 1, 128),
-          (1, 1, 1, 300, 64), (1, 2, 500, 777, 128), (1, 2, 129, 300, 32), (1, 1, 200, 300, 256)]
+          (1, 1, 1, 300, 64), (1, 2, 500, 777, 128), (1, 2, 129, 300, 32), (1, 1, 200, 300, 256),
+          (1, 2, 200, 300, 96)]
 
 
 @pytest.mark.parametrize("causal", [False, True])

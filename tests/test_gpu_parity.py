@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import flashattention_forward_fwd_amd as fa
-from flashattention_forward_fwd_amd.inputs import (WORKLOADS, head_row_samples, random_qkv,
+from flashattention_forward_fwd_amd.inputs import (WORKLOADS, head_row_samples, random_qkv, sample_rows,
                                                    workload_inputs)
 from oracle import ref
 from tests.parity import TOL, check_case, compare, run_gpu, say, widen
@@ -82,6 +82,24 @@ def test_parity_head_dim_256(shape, causal):
     check_case("d256 %s" % (shape,), q, k, v, causal, float(np.float32(1 / np.sqrt(d))), "bf16")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 200, 300, 96), (2, 1, 129, 129, 96), (1, 1, 1, 70, 96),
+                                   (1, 2, 333, 1000, 96)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_parity_head_dim_96(shape, causal):
+    """d = 96 (bf16: 192-byte rows staged as 256-byte LDS rows, upper chunks unused)."""
+    B, H, Lq, Lk, d = shape
+    q, k, v = random_qkv(B, H, Lq, Lk, d, "bf16", seed=sum(shape) + 3 * causal)
+    check_case("d96 %s" % (shape,), q, k, v, causal, float(np.float32(1 / np.sqrt(d))), "bf16")
+
+
+def test_parity_head_dim_96_long_sampled():
+    """d = 96 at N=4096 (B=2, H=16, causal), 256 sampled rows of every head."""
+    q, k, v = random_qkv(2, 16, 4096, 4096, 96, "bf16", seed=961)
+    rows = sample_rows(4096, 256, 962)
+    check_case("d96 long", q, k, v, True, float(np.float32(1 / np.sqrt(96))), "bf16", rows=rows)
+
+
 def test_pages_selfcheck_recipe_through_kernel():
     """The pages' NumPy self-check recipe (rng(0) normal, 100 x 32 for Q, K, V): the
     same draws, rounded to bf16 (and kept fp32), through the kernels."""
@@ -148,7 +166,7 @@ def test_bitwise_repeatable():
 
 
 def test_error_paths_on_device():
-    q = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(1, 1, 8, 80, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(fa.FA2Error) as e:
         fa.forward(q, q, q)
     assert e.value.status == 3

@@ -35,6 +35,7 @@ SHAPES = [
     (1, 2, 300, 5000, 128),
     (1, 2, 200, 700, 32),
     (1, 1, 150, 900, 256),
+    (1, 2, 150, 900, 96),
 ]
 
 
@@ -132,7 +133,7 @@ def test_splitkv_workspace_too_small():
 
 
 # ------------------------------------------------------ stand-alone merge kernel
-@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 def test_merge_partials_matches_oracle(d):
     """Partials: the oracle's attention over key shards (rounded to fp32), plus one
     part that is empty (-inf, NaN output) for every row and one empty for some rows."""

@@ -49,6 +49,7 @@ CASES = [
     (1, 1, 129, 1000, 128, 5, 900),
     (1, 2, 300, 300, 32, 20, 0),
     (1, 1, 300, 400, 256, 50, 10),
+    (1, 2, 300, 500, 96, 40, 5),
 ]
 
 
