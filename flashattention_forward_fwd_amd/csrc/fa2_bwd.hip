@@ -89,16 +89,21 @@ constexpr int kRowTile = 64;                      // dK/dV: query rows per LDS t
 //    (the transposed A operand): the 4 rows land in 4 different aligned groups
 //    of 4 chunks, so the 16 (row, chunk) pairs are 16 different chunks.
 // For d = 64 two rows, for d = 32 four rows share one 256-byte line; the row
-// within the line separates them.
+// within the line separates them.  d = 96: a 192-byte row takes a d = 128 row
+// (256 bytes) in LDS, with the d = 128 swizzle; the chunks past column 95 are
+// neither loaded nor read.
 template <int D> struct BTile {
-    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kLdsD = D == 96 ? 128 : D;          // row length in LDS
+    static constexpr int kRowBytes = 2 * kLdsD;              // LDS row
+    static constexpr int kGRowBytes = 2 * D;                 // HBM row
     static constexpr int kChunks = kRowBytes / 16;
+    static constexpr int kGChunks = kGRowBytes / 16;         // chunks that hold data
     static constexpr int kRowsPerXfer = 1024 / kRowBytes;   // rows per 1 KiB DMA transfer
     static __device__ __forceinline__ int swz(int r)
     {
-        return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
-             : D == 64  ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
-                        : ((r >> 2) & 3);
+        return kLdsD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+             : kLdsD == 64  ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
+                            : ((r >> 2) & 3);
     }
     // Byte address in the tile of logical byte x of row r.
     static __device__ __forceinline__ int addr(int r, int x)
@@ -124,10 +129,11 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t src, int row0, 
     for (int x = 0; x < kPerWave; ++x) {
         const int b = wave * kPerWave + x;
         const int r = b * T::kRowsPerXfer + lane / T::kChunks;
-        const int phys = lane % T::kChunks;
+        const int logical = (lane % T::kChunks) ^ T::swz(r);
         // The whole offset goes in the VGPR operand, which the range check covers.
-        const int voff = (row0 + r) * T::kRowBytes + 16 * (phys ^ T::swz(r));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void *)(dst + b * 512), 16, voff, 0, 0, 0);
+        const int voff = (row0 + r) * T::kGRowBytes + 16 * logical;
+        if (T::kGChunks == T::kChunks || logical < T::kGChunks)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (LDS_AS void *)(dst + b * 512), 16, voff, 0, 0, 0);
     }
 }
 
@@ -181,17 +187,20 @@ __device__ __forceinline__ void store_tokens(uint16_t *dst_row, const f32x16 (&a
 }
 
 // ---------------------------------------------------------------- 1. prep
-// D_i = sum_t dO_it O_it (fp32) and lse2_i = lse_i * log2(e); D/8 threads per row.
+// D_i = sum_t dO_it O_it (fp32) and lse2_i = lse_i * log2(e); D/8 threads per row
+// (a power of two for the butterfly sum: d = 96 takes 16, the last 4 idle).
+template <int D> constexpr int kPrepThreadsPerRow = D == 96 ? 16 : D / 8;
+
 template <int D, typename E>
 __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, const uint16_t *dout, const float *lse,
                                                            float *lse2, float *delta, int64_t rows, float dmul)
 {
-    constexpr int kTpr = D / 8;
+    constexpr int kTpr = kPrepThreadsPerRow<D>;
     const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t row = gid / kTpr;
     const int part = (int)(gid % kTpr);
     float acc = 0.f;
-    if (row < rows) {
+    if (row < rows && part < D / 8) {
         const f32x8 a = __builtin_convertvector(*reinterpret_cast<const typename V16<E>::x8 *>(o + row * D + 8 * part), f32x8);
         const f32x8 b = __builtin_convertvector(*reinterpret_cast<const typename V16<E>::x8 *>(dout + row * D + 8 * part), f32x8);
 #pragma unroll
@@ -233,7 +242,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     using e8 = typename V16<E>::x8;
     constexpr int kDc = D / 16;
     constexpr int kDt = D / 32;
-    constexpr int kTileElems = kRowTile * D;
+    constexpr int kTileElems = kRowTile * T::kLdsD;
     __shared__ __attribute__((aligned(1024))) uint16_t sQ0[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sQ1[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sQ2[kTileElems];
@@ -284,9 +293,9 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 
     const size_t row_off = (size_t)bh * p.Lq;
     const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const uint16_t *>(p.q) + row_off * D), 0, p.Lq * T::kRowBytes, kRawBufferFlags);
+        (void *)(static_cast<const uint16_t *>(p.q) + row_off * D), 0, p.Lq * T::kGRowBytes, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const uint16_t *>(p.dout) + row_off * D), 0, p.Lq * T::kRowBytes, kRawBufferFlags);
+        (void *)(static_cast<const uint16_t *>(p.dout) + row_off * D), 0, p.Lq * T::kGRowBytes, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(p.lse2 + row_off), 0, p.Lq * 4, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
@@ -453,7 +462,7 @@ void fa2_bwd_dq_kernel(BwdParams p)
     using e8 = typename V16<E>::x8;
     constexpr int kDc = D / 16;
     constexpr int kDt = D / 32;
-    constexpr int kTileElems = kBc * D;
+    constexpr int kTileElems = kBc * T::kLdsD;
     __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sV0[kTileElems];
@@ -484,9 +493,9 @@ void fa2_bwd_dq_kernel(BwdParams p)
 
     const size_t kv_off = (size_t)bh * p.Lk * D;
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const uint16_t *>(p.k) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+        (void *)(static_cast<const uint16_t *>(p.k) + kv_off), 0, p.Lk * T::kGRowBytes, kRawBufferFlags);
     const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const uint16_t *>(p.v) + kv_off), 0, p.Lk * T::kRowBytes, kRawBufferFlags);
+        (void *)(static_cast<const uint16_t *>(p.v) + kv_off), 0, p.Lk * T::kGRowBytes, kRawBufferFlags);
 
     const int q0 = qt * kBr + wave * kRowsPerWave;
     const int qrow = q0 + l32;
@@ -653,7 +662,7 @@ template <int D, typename E, bool DROPOUT = false>
 hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const void *o, const float *lse,
                         hipStream_t stream)
 {
-    const int64_t threads = rows * (D / 8);
+    const int64_t threads = rows * kPrepThreadsPerRow<D>;
     hipLaunchKernelGGL((fa2_bwd_prep_kernel<D, E>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(p.dout), lse,
                        const_cast<float *>(p.lse2), const_cast<float *>(p.delta), rows,
@@ -680,7 +689,7 @@ hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
-    with_head_dim(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, __bf16>(p, masked, rows, o, lse, stream); });
+    with_head_dim<true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, __bf16>(p, masked, rows, o, lse, stream); });
     return err;
 }
 
@@ -689,7 +698,7 @@ hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float 
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
-    with_head_dim(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, _Float16>(p, masked, rows, o, lse, stream); });
+    with_head_dim<true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, _Float16>(p, masked, rows, o, lse, stream); });
     return err;
 }
 
@@ -698,7 +707,7 @@ hipError_t launch_bwd_bf16_dropout(const BwdParams &p, int d, const void *o, con
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
-    with_head_dim(d, [&](auto dim) {
+    with_head_dim<true>(d, [&](auto dim) {
         err = launch_bwd_d<decltype(dim)::value, __bf16, true>(p, masked, rows, o, lse, stream);
     });
     return err;

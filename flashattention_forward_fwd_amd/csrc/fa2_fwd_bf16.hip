@@ -598,7 +598,7 @@ template <bool SPLIT, typename E = __bf16>
 hipError_t launch(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    with_head_dim<true>(d, [&](auto dim) {
+    with_head_dim<true, true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, SPLIT, false, E>), grid, block, 0, stream, p);
         else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, SPLIT, false, E>), grid, block, 0, stream, p);
@@ -626,7 +626,7 @@ hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t st
 hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    with_head_dim<true>(d, [&](auto dim) {
+    with_head_dim<true, true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, stream, p);
     });
@@ -636,7 +636,7 @@ hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
 hipError_t launch_fwd_bf16_dropout(const FwdParams &p, int d, bool causal, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
-    with_head_dim<true>(d, [&](auto dim) {
+    with_head_dim<true, true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         if (causal)
             hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, false, false, __bf16, true>), grid, block, 0, stream, p);

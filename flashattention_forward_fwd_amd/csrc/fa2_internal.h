@@ -117,15 +117,16 @@ __device__ __forceinline__ float halves_sum(float x)
 // Host-side launchers (one per element type), defined next to their kernels.
 namespace fa2 {
 // Calls f(std::integral_constant<int, D>{}) for the head dimension d: 32, 64,
-// 128, and 96 and 256 where FWD16 (the bf16/fp16 forward kernels and the
-// merge); the entry points reject every other value before a launch.
-template <bool FWD16 = false, typename F>
+// 128, 96 where WITH_96 (the 16-bit forward and backward kernels and the
+// merge) and 256 where WITH_256 (the 16-bit forward kernels and the merge); the
+// entry points reject every other value before a launch.
+template <bool WITH_96 = false, bool WITH_256 = false, typename F>
 inline void with_head_dim(int d, F f)
 {
     if (d == 32) f(std::integral_constant<int, 32>{});
     else if (d == 64) f(std::integral_constant<int, 64>{});
-    else if (FWD16 && d == 96) f(std::integral_constant<int, FWD16 ? 96 : 128>{});
-    else if (FWD16 && d == 256) f(std::integral_constant<int, FWD16 ? 256 : 128>{});
+    else if (WITH_96 && d == 96) f(std::integral_constant<int, WITH_96 ? 96 : 128>{});
+    else if (WITH_256 && d == 256) f(std::integral_constant<int, WITH_256 ? 256 : 128>{});
     else f(std::integral_constant<int, 128>{});
 }
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t stream);

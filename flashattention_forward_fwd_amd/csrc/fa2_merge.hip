@@ -67,7 +67,7 @@ hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_part
     const int64_t threads = rows * (d / 4);
     const dim3 grid((unsigned)((threads + kMergeThreads - 1) / kMergeThreads)), block(kMergeThreads);
     uint16_t *ob = static_cast<uint16_t *>(o);
-    with_head_dim<true>(d, [&](auto dim) {
+    with_head_dim<true, true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         hipLaunchKernelGGL((fa2_merge_kernel<D>), grid, block, 0, stream, o_parts, lse_parts, n_parts, rows, ob, lse);
     });

@@ -143,7 +143,8 @@ def test_bwd_rejects_before_touching_the_device():
     assert f(*args(do=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
     assert f(*args(dk=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
     assert f(*args(q=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
-    assert f(*args(), 1, 1, 8, 8, 96, 0.1, 0, A, big, None) == 3
+    assert f(*args(), 1, 1, 8, 8, 80, 0.1, 0, A, big, None) == 3
+    assert f(*args(), 1, 1, 8, 8, 256, 0.1, 0, A, big, None) == 3
     assert f(*args(), 1, 1, 0, 8, 64, 0.1, 0, A, big, None) == 2
     assert f(*args(), 1, 1, 8, 8, 64, 0.1, 2, A, big, None) == 4
     assert f(*args(dv=A + 2), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 5

@@ -60,6 +60,9 @@ SHAPES = [
     (2, 2, 384, 384, 128),
     (1, 2, 129, 129, 32),
     (1, 1, 300, 200, 32),
+    (1, 2, 129, 129, 96),
+    (2, 1, 300, 511, 96),
+    (1, 1, 1, 300, 96),
 ]
 
 
@@ -101,6 +104,24 @@ def test_bwd_parity_workload(name):
                                      rows=rows, keys=keys)
         got = (dq[b, h, rows][None, None], dk[b, h, keys][None, None], dv[b, h, keys][None, None])
         compare_grads("%s head (%d,%d)" % (name, b, h), got, want)
+
+
+def test_bwd_parity_d96_long():
+    """d = 96 at N=4096 (B=2, H=16, causal); 2 heads, 256 sampled rows and keys each."""
+    B, H, L, d = 2, 16, 4096, 96
+    q, k, v = random_qkv(B, H, L, L, d, "bf16", seed=963)
+    do = random_dout(B, H, L, d, "bf16", seed=963)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    say("case d96 long (bwd)")
+    dq, dk, dv = gpu_grads(q, k, v, do, True, scale)
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        rows = sample_rows(L, 256, 964 + b * H + h)
+        keys = sample_rows(L, 256, 965 + b * H + h)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        want = ref.attention_bwd_f64(widen(q[sl]), widen(k[sl]), widen(v[sl]), widen(do[sl]), scale, True,
+                                     rows=rows, keys=keys)
+        got = (dq[b, h, rows][None, None], dk[b, h, keys][None, None], dv[b, h, keys][None, None])
+        compare_grads("d96 long head (%d,%d)" % (b, h), got, want)
 
 
 def test_bwd_closed_forms():

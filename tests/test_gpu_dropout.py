@@ -177,6 +177,7 @@ BWD_CASES = [
     (2, 2, 129, 1000, 128, False, 0.05),
     (1, 1, 640, 640, 128, True, 0.3),
     (1, 1, 333, 129, 64, True, 0.6),
+    (1, 2, 300, 257, 96, False, 0.25),
 ]
 
 
@@ -199,7 +200,8 @@ def test_dropout_backward_zero_rate_is_plain_backward():
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("d,Lq,causal", [(128, 128, False), (128, 100, True), (64, 64, False), (32, 32, True)])
+@pytest.mark.parametrize("d,Lq,causal", [(128, 128, False), (128, 100, True), (64, 64, False), (32, 32, True),
+                                         (96, 96, False)])
 def test_dropout_backward_mask_exact(d, Lq, causal):
     """dout = I (Lq <= d): dv[j, i] = (256 / t) P[i, j] Z[i, j], so the nonzero
     pattern of dv[..., :Lq] is the transposed keep mask (and the causal mask) bit

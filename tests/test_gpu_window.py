@@ -95,6 +95,7 @@ BWD_CASES = [
     (1, 2, 384, 512, 128, -1, 50),
     (1, 1, 640, 640, 64, 127, -1),
     (1, 2, 300, 300, 32, 20, 3),
+    (1, 2, 300, 400, 96, 50, 0),
 ]
 
 
