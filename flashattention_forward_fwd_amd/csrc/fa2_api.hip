@@ -70,15 +70,13 @@ bool product_fits(int64_t a, int64_t b, int64_t c, int64_t d)
     return a <= lim / d;
 }
 
-// Head-dimension sets: the fp32 forward (32, 64, 128), the backward (also 96),
-// the 16-bit forward kernels and the merge (also 96 and 256).
-enum DimSet { kDimsF32, kDimsBwd, kDimsFwd16 };
+// Head-dimension sets: the fp32 forward (32, 64, 128) and every 16-bit kernel
+// and the merge (also 96 and 256).
+enum DimSet { kDimsF32, kDims16 };
 bool head_dim_ok(int d, DimSet dims)
 {
     if (d == 32 || d == 64 || d == 128) return true;
-    if (d == 96) return dims != kDimsF32;
-    if (d == 256) return dims == kDimsFwd16;
-    return false;
+    return dims == kDims16 && (d == 96 || d == 256);
 }
 
 int prepare(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -195,12 +193,13 @@ int prepare_bwd(const void *q, const void *k, const void *v, const void *o, cons
                 fa2::BwdParams *out)
 {
     if (!dout || !dq || !dk || !dv) return FA2_ERR_NULL;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, nullptr, kDimsBwd);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, nullptr, kDims16);
     if (st != FA2_OK) return st;
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return FA2_ERR_ALIGN;
     // Query tiles of one head are addressed with 32-bit buffer offsets too.
     if (((int64_t)Lq + fa2::kBr) * d * 2 > INT32_MAX) return FA2_ERR_DIM;
-    const int64_t key_blocks = (Lk + 127) / 128;
+    const int64_t key_block = d == 256 ? 64 : 128;    // keys per dK/dV work-group
+    const int64_t key_blocks = (Lk + key_block - 1) / key_block;
     if ((int64_t)B * H > INT32_MAX / key_blocks) return FA2_ERR_DIM;          // dK/dV grid
     const int64_t rows = (int64_t)B * H * Lq;
     if (rows * (d == 96 ? 16 : d / 8) / 256 + 1 > INT32_MAX) return FA2_ERR_DIM;  // prep grid
@@ -235,14 +234,14 @@ int fa2_check_args(const void *q, const void *k, const void *v, const void *o, c
                    int B, int H, int Lq, int Lk, int d, float scale, int causal, int elem_bytes)
 {
     return prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes, nullptr,
-                   elem_bytes == 2 ? kDimsFwd16 : kDimsF32);
+                   elem_bytes == 2 ? kDims16 : kDimsF32);
 }
 
 int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
             int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDimsFwd16);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     if (fa2::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -254,7 +253,7 @@ int fa2_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDimsFwd16);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     if (fa2::launch_fwd_f16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -279,7 +278,7 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
                    void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 2, &p, kDimsFwd16);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 2, &p, kDims16);
     if (st != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
     // Negative bounds all mean "unbounded"; keep them as -1.
@@ -295,7 +294,7 @@ int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float 
                     double dropout_p, uint64_t seed, uint32_t offset, void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDimsFwd16);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
     if (st != FA2_OK) return st;
     if ((st = dropout_setup(dropout_p, seed, offset, &p.drop)) != FA2_OK) return st;
     if ((st = check_device()) != FA2_OK) return st;
@@ -306,7 +305,7 @@ int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float 
 
 int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal)
 {
-    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || !head_dim_ok(d, kDimsFwd16)) return 1;
+    if (B <= 0 || H <= 0 || Lq <= 0 || Lk <= 0 || !head_dim_ok(d, kDims16)) return 1;
     return auto_splits(B, H, Lq, Lk, causal);
 }
 
@@ -315,7 +314,7 @@ size_t fa2_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int caus
     // Size checks of fa2_fwd_splitkv, on stand-in aligned pointers.
     const void *fake = reinterpret_cast<const void *>(uintptr_t(256));
     if (prepare(fake, fake, fake, fake, static_cast<const float *>(fake), B, H, Lq, Lk, d, 1.0f,
-                causal, 2, nullptr, kDimsFwd16) != FA2_OK)
+                causal, 2, nullptr, kDims16) != FA2_OK)
         return 0;
     if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return 0;
     const int S = num_splits == 0 ? auto_splits(B, H, Lq, Lk, causal) : num_splits;
@@ -327,7 +326,7 @@ int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float 
                     int num_splits, void *workspace, size_t workspace_bytes_given, void *stream)
 {
     fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDimsFwd16);
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
     if (st != FA2_OK) return st;
     if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return FA2_ERR_ARG;
     if (!workspace) return FA2_ERR_WORKSPACE;
@@ -364,7 +363,7 @@ int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts
     if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL;
     if (n_parts < 1 || n_parts > FA2_MAX_SPLITS) return FA2_ERR_ARG;
     if (rows < 1) return FA2_ERR_DIM;
-    if (!head_dim_ok(d, kDimsFwd16)) return FA2_ERR_UNSUPPORTED_D;
+    if (!head_dim_ok(d, kDims16)) return FA2_ERR_UNSUPPORTED_D;
     if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
         return FA2_ERR_ALIGN;
     if (!product_fits(n_parts, rows, d, sizeof(float))) return FA2_ERR_DIM;
@@ -449,7 +448,7 @@ const char *fa2_status_string(int status)
     case FA2_OK: return "ok";
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
     case FA2_ERR_DIM: return "B, H, Lq, Lk must be positive and the sizes must fit (one head's K below 2 GiB)";
-    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128 (or 96 for 16-bit data, or 256 for the 16-bit forward)";
+    case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128 (or 96 or 256 for 16-bit data)";
     case FA2_ERR_ARG: return "causal must be 0 or 1 and scale finite and positive";
     case FA2_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";

@@ -78,8 +78,6 @@ constexpr int kRawBufferFlags = 0x00020000;   // raw buffer access, gfx9 resourc
 constexpr float kLog2e = 1.44269504088896340736f;
 
 constexpr int kKeysPerWave = 32;                  // dK/dV: keys owned by one wavefront
-constexpr int kKeyBlock = kWaves * kKeysPerWave;  // dK/dV: keys per work-group
-constexpr int kRowTile = 64;                      // dK/dV: query rows per LDS tile
 
 // A row-major bf16 tile [rows][D] in LDS, its 16-byte chunks XOR-swizzled by
 // row.  The swizzle serves both read patterns the backward uses:
@@ -89,7 +87,8 @@ constexpr int kRowTile = 64;                      // dK/dV: query rows per LDS t
 //    (the transposed A operand): the 4 rows land in 4 different aligned groups
 //    of 4 chunks, so the 16 (row, chunk) pairs are 16 different chunks.
 // For d = 64 two rows, for d = 32 four rows share one 256-byte line; the row
-// within the line separates them.  d = 96: a 192-byte row takes a d = 128 row
+// within the line separates them; for d = 256 the swizzle moves a chunk within
+// the first or second 256 bytes of its row.  d = 96: a 192-byte row takes a d = 128 row
 // (256 bytes) in LDS, with the d = 128 swizzle; the chunks past column 95 are
 // neither loaded nor read.
 template <int D> struct BTile {
@@ -101,7 +100,7 @@ template <int D> struct BTile {
     static constexpr int kRowsPerXfer = 1024 / kRowBytes;   // rows per 1 KiB DMA transfer
     static __device__ __forceinline__ int swz(int r)
     {
-        return kLdsD == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+        return kLdsD >= 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
              : kLdsD == 64  ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
                             : ((r >> 2) & 3);
     }
@@ -231,17 +230,33 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
 // SIMD with nothing to hide its latencies.  The one-step lag keeps a single
 // barrier per step: Q/dO tiles are triple-buffered (t + 1 loading, t read by
 // the dV wavefronts, t - 1 by the dK wavefronts) and P double-buffered.
-constexpr int kDkdvWaves = 8;
-constexpr int kDkdvThreads = kDkdvWaves * kWave;
+//
+// d = 256: a wavefront's K (or V) of 32 keys and its accumulator take 192
+// registers, so the work-group shrinks to four wavefronts (two key groups, 64
+// keys), one per SIMD with the accumulation registers in use, and the Q / dO
+// tiles to 32 rows (the six tiles then take 96 KiB of LDS).
+template <int D> struct DkdvShape {
+    static constexpr bool kWide = D == 256;
+    static constexpr int kWaves = kWide ? 4 : 8;              // wavefronts per work-group
+    static constexpr int kGroups = kWaves / 2;                 // 32-key groups (one dV, one dK wave each)
+    static constexpr int kKeyBlock = kGroups * kKeysPerWave;   // keys per work-group
+    static constexpr int kRowTile = kWide ? 32 : 64;           // query rows per LDS tile
+    static constexpr int kHalves = kRowTile / 32;              // 32-row score tiles per row tile
+    static constexpr int kPChunks = kRowTile / 16;             // 16-row operand chunks per row tile
+    static constexpr int kThreads = kWaves * kWave;
+};
 
 template <int D, bool MASKED, typename E, bool DROPOUT>
-__global__ __launch_bounds__(kDkdvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(DkdvShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
 void fa2_bwd_dkdv_kernel(BwdParams p)
 {
     using T = BTile<D>;
+    using S = DkdvShape<D>;
     using e8 = typename V16<E>::x8;
     constexpr int kDc = D / 16;
     constexpr int kDt = D / 32;
+    constexpr int kRowTile = S::kRowTile;
+    constexpr int kKeyBlock = S::kKeyBlock;
     constexpr int kTileElems = kRowTile * T::kLdsD;
     __shared__ __attribute__((aligned(1024))) uint16_t sQ0[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sQ1[kTileElems];
@@ -250,9 +265,10 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     __shared__ __attribute__((aligned(1024))) uint16_t sO1[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sO2[kTileElems];
     // P of one tile: [key group][chunk c][lane] x 16 bytes, in the lane order of the B operand
-    __shared__ __attribute__((aligned(1024))) e8 sP0[kWaves * 4 * kWave];
-    __shared__ __attribute__((aligned(1024))) e8 sP1[kWaves * 4 * kWave];
-    // per buffer: lse2 of the tile's 64 rows, then their D
+    __shared__ __attribute__((aligned(1024))) e8 sP0[S::kGroups * S::kPChunks * kWave];
+    __shared__ __attribute__((aligned(1024))) e8 sP1[S::kGroups * S::kPChunks * kWave];
+    // per buffer: lse2 of the tile's rows at 0, their D at 64 (a 32-row tile
+    // leaves the upper halves unused)
     __shared__ __attribute__((aligned(256))) float sStat0[128];
     __shared__ __attribute__((aligned(256))) float sStat1[128];
     __shared__ __attribute__((aligned(256))) float sStat2[128];
@@ -262,8 +278,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     const int lane = tid % kWave;
     const int l32 = lane & 31;
     const int hh = lane >> 5;
-    const bool is_dk = wave >= kWaves;              // wave-uniform role
-    const int grp = wave % kWaves;                  // 32-key group
+    const bool is_dk = wave >= S::kGroups;          // wave-uniform role
+    const int grp = wave % S::kGroups;              // 32-key group
 
     const int n_bh = p.B * p.H;
     const int bh = blockIdx.x % n_bh;
@@ -308,8 +324,8 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     auto sbuf = [&](int slot) { return slot == 0 ? sStat0 : slot == 1 ? sStat1 : sStat2; };
     auto load = [&](int t) {
         const int slot = (t - t0) % 3;
-        load_tile<D, kRowTile, kDkdvWaves>(rQ, t * kRowTile, qbuf(slot), wave, lane);
-        load_tile<D, kRowTile, kDkdvWaves>(rO, t * kRowTile, obuf(slot), wave, lane);
+        load_tile<D, kRowTile, S::kWaves>(rQ, t * kRowTile, qbuf(slot), wave, lane);
+        load_tile<D, kRowTile, S::kWaves>(rO, t * kRowTile, obuf(slot), wave, lane);
         if (wave < 2)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rL : rD, (LDS_AS void *)(sbuf(slot) + 64 * wave),
                                                      4, 4 * (t * kRowTile + lane), 0, 0, 0);
@@ -342,11 +358,11 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
                 const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
                 const LDS_AS float *st = (const LDS_AS float *)sbuf(slot);
-                // S = Q K^T for 64 rows (two 32-row halves h) x this group's 32
+                // S = Q K^T for the tile's rows (32-row halves h) x this group's 32
                 // keys.  Entry i of half h is row 32h + 8(i/4) + 4hh + i%4.
-                f32x16 s[2];
+                f32x16 s[S::kHalves];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < S::kHalves; ++h) {
                     s[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
@@ -358,12 +374,15 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                                 (p.wr < 0 || (int64_t)kw0 + kKeysPerWave - 1 <= (int64_t)t * kRowTile + p.wr));
                 // Chunk c (B operand of the products over the tile's rows) holds
                 // rows 16c + 8(e/4) + 4hh + e%4, e = 0..7: entries 8(c%2) + e of half c/2.
-                LDS_AS e8 *pdst = (LDS_AS e8 *)((t & 1) ? sP1 : sP0) + grp * 4 * kWave;
+                LDS_AS e8 *pdst = (LDS_AS e8 *)((t & 1) ? sP1 : sP0) + grp * S::kPChunks * kWave;
                 DropMask mk;
-                if (DROPOUT) mk = mask_key_lanes(p.drop, t * kRowTile, key, lane, bh);
-                e8 pf[4];
+                if (DROPOUT)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                    for (int h = 0; h < S::kHalves; ++h)
+                        mk.y[h] = mask_key_lanes_one(p.drop, t * kRowTile, h, key, lane, bh);
+                e8 pf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
                     const int h = c >> 1, i0 = 8 * (c & 1);
                     const f32x4 l4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 4 * hh);
                     const f32x4 l4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 8 + 4 * hh);
@@ -393,7 +412,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < S::kPChunks; ++c)
                         acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, dt, c, lane), pf[c], acc[dt]);
             }
         } else {
@@ -404,18 +423,18 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
                 const LDS_AS float *st = (const LDS_AS float *)sbuf(slot);
                 // dP = dO V^T, same layout as S.
-                f32x16 dp[2];
+                f32x16 dp[S::kHalves];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < S::kHalves; ++h) {
                     dp[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
                         dp[h] = mfma_32x32x16(read_rows_op<D, E>(ob, 32 * h + l32, c, hh), xf[c], dp[h]);
                 }
-                const LDS_AS e8 *psrc = (const LDS_AS e8 *)((tk & 1) ? sP1 : sP0) + grp * 4 * kWave;
-                e8 dsf[4];
+                const LDS_AS e8 *psrc = (const LDS_AS e8 *)((tk & 1) ? sP1 : sP0) + grp * S::kPChunks * kWave;
+                e8 dsf[S::kPChunks];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                for (int c = 0; c < S::kPChunks; ++c) {
                     const int h = c >> 1, i0 = 8 * (c & 1);
                     const e8 pc = psrc[c * kWave + lane];
                     const f32x4 d4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 4 * hh);
@@ -437,7 +456,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < S::kPChunks; ++c)
                         acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, dt, c, lane), dsf[c], acc[dt]);
             }
         }
@@ -454,8 +473,11 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------- 3. dQ
+// d = 256: Q, dO and the dQ accumulator take 256 registers, so that instance runs
+// one wavefront per SIMD with the accumulation registers in use (and one
+// work-group per CU: 128 KiB of LDS), as the d = 256 forward.
 template <int D, bool MASKED, typename E, bool DROPOUT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
 void fa2_bwd_dq_kernel(BwdParams p)
 {
     using T = BTile<D>;
@@ -668,12 +690,14 @@ hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const voi
                        const_cast<float *>(p.lse2), const_cast<float *>(p.delta), rows,
                        DROPOUT ? 1.0f / p.drop.keep_scale : 1.0f);
     BwdParams pk = p;
-    pk.n_blocks = (p.Lk + kKeyBlock - 1) / kKeyBlock;
+    pk.n_blocks = (p.Lk + DkdvShape<D>::kKeyBlock - 1) / DkdvShape<D>::kKeyBlock;
     pk.n_wg = pk.n_blocks * p.B * p.H;
     if (masked)
-        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true, E, DROPOUT>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true, E, DROPOUT>), dim3(pk.n_wg), dim3(DkdvShape<D>::kThreads), 0,
+                           stream, pk);
     else
-        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false, E, DROPOUT>), dim3(pk.n_wg), dim3(kDkdvThreads), 0, stream, pk);
+        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false, E, DROPOUT>), dim3(pk.n_wg), dim3(DkdvShape<D>::kThreads), 0,
+                           stream, pk);
     BwdParams pq = p;
     pq.n_blocks = (p.Lq + kBr - 1) / kBr;
     pq.n_wg = pq.n_blocks * p.B * p.H;
@@ -689,7 +713,7 @@ hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
-    with_head_dim<true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, __bf16>(p, masked, rows, o, lse, stream); });
+    with_head_dim<true, true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, __bf16>(p, masked, rows, o, lse, stream); });
     return err;
 }
 
@@ -698,7 +722,7 @@ hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float 
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
-    with_head_dim<true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, _Float16>(p, masked, rows, o, lse, stream); });
+    with_head_dim<true, true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, _Float16>(p, masked, rows, o, lse, stream); });
     return err;
 }
 
@@ -707,7 +731,7 @@ hipError_t launch_bwd_bf16_dropout(const BwdParams &p, int d, const void *o, con
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
-    with_head_dim<true>(d, [&](auto dim) {
+    with_head_dim<true, true>(d, [&](auto dim) {
         err = launch_bwd_d<decltype(dim)::value, __bf16, true>(p, masked, rows, o, lse, stream);
     });
     return err;

@@ -137,17 +137,13 @@ __device__ __forceinline__ DropMask mask_query_lanes(const DropoutParams &dp, in
 // lane of a quad draws the block of one 4-row group; its bytes are transposed
 // within the lane (word w byte b -> word b byte w: the 4 rows of key b) and then
 // across the quad, so every lane gets the rows of its own key.
-__device__ __forceinline__ DropMask mask_key_lanes(const DropoutParams &dp, int r0, int key, int lane, int bh)
+__device__ __forceinline__ u32x4_t mask_key_lanes_one(const DropoutParams &dp, int r0, int t, int key, int lane,
+                                                      int bh)
 {
-    DropMask mk;
     const int s = lane & 3, hh = lane >> 5;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const uint32_t rblock = (uint32_t)(r0 / 4 + 8 * t + 2 * s + hh);
-        mk.y[t] = quad_transpose(byte_transpose(philox4x32_10((uint32_t)key / 4u, rblock, (uint32_t)bh, dp.offset,
-                                                              dp.seed_lo, dp.seed_hi)), s);
-    }
-    return mk;
+    const uint32_t rblock = (uint32_t)(r0 / 4 + 8 * t + 2 * s + hh);
+    return quad_transpose(byte_transpose(philox4x32_10((uint32_t)key / 4u, rblock, (uint32_t)bh, dp.offset,
+                                                       dp.seed_lo, dp.seed_hi)), s);
 }
 
 }  // namespace fa2

@@ -29,12 +29,10 @@
  * no row is empty.  Key blocks that are masked for every row of a Q block are
  * skipped ("FlashAttention 怎么做?", section "FlashAttention-2 改了什么").
  *
- * Head dimension d: 32, 64 or 128 everywhere; 96 also for every bf16 / fp16 entry
- * point (forward, backward, merge; not fa2_fwd_f32); 256 for the bf16 and fp16
- * forward entry points (fa2_fwd, fa2_fwd_f16, fa2_fwd_window, fa2_fwd_dropout,
- * fa2_fwd_splitkv) and fa2_merge_partials.  The d = 256 kernels run one wavefront
- * per SIMD; d = 96 rows take d = 128 rows in on-chip memory (the extra columns are
- * neither loaded nor read).
+ * Head dimension d: 32, 64 or 128 everywhere; 96 and 256 also for every bf16 / fp16
+ * entry point (forward, backward, merge; not fa2_fwd_f32).  The d = 256 kernels run
+ * one wavefront per SIMD; d = 96 rows take d = 128 rows in on-chip memory (the extra
+ * columns are neither loaded nor read).
  *
  * Layout: every tensor is dense, row-major, without strides:
  *     q, o   [B, H, Lq, d]      k, v   [B, H, Lk, d]      lse   [B, H, Lq]  fp32
@@ -69,9 +67,8 @@ typedef enum fa2_status {
     FA2_ERR_DIM = 2,             /* B, H, Lq or Lk <= 0, an element count overflows int64, the
                                     grid does not fit, or (Lk + 64) * d * element size of one
                                     head's K exceeds 2^31 - 1 bytes */
-    FA2_ERR_UNSUPPORTED_D = 3,   /* head dimension d not in {32, 64, 128}, or 96 for the
-                                    bf16/fp16 entry points, or 256 for the bf16/fp16 forward
-                                    entry points and the merge */
+    FA2_ERR_UNSUPPORTED_D = 3,   /* head dimension d not in {32, 64, 128}, or 96 / 256 for
+                                    the bf16/fp16 entry points and the merge */
     FA2_ERR_ARG = 4,             /* causal not 0 or 1, or scale not finite or <= 0 */
     FA2_ERR_ALIGN = 5,           /* a tensor pointer is not 16-byte aligned */
     FA2_ERR_DEVICE = 6,          /* no usable HIP device, or the device is not gfx950 */

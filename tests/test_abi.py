@@ -59,7 +59,7 @@ def test_argument_checks(elem):
     assert st(B=1 << 30, H=1 << 30) == 2
     for d in (0, 16, 80, 112, 512, 127):
         assert st(d=d) == 3
-    assert st(d=256) == (0 if elem == 2 else 3)      # d = 96, 256: 16-bit forward only
+    assert st(d=256) == (0 if elem == 2 else 3)      # d = 96, 256: 16-bit data only
     assert st(d=96) == (0 if elem == 2 else 3)
     assert st(causal=2) == 4 and st(causal=-1) == 4
     assert st(scale=0.0) == 4 and st(scale=-1.0) == 4
@@ -144,7 +144,7 @@ def test_bwd_rejects_before_touching_the_device():
     assert f(*args(dk=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
     assert f(*args(q=None), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 1
     assert f(*args(), 1, 1, 8, 8, 80, 0.1, 0, A, big, None) == 3
-    assert f(*args(), 1, 1, 8, 8, 256, 0.1, 0, A, big, None) == 3
+    assert f(*args(), 1, 1, 8, 8, 512, 0.1, 0, A, big, None) == 3
     assert f(*args(), 1, 1, 0, 8, 64, 0.1, 0, A, big, None) == 2
     assert f(*args(), 1, 1, 8, 8, 64, 0.1, 2, A, big, None) == 4
     assert f(*args(dv=A + 2), 1, 1, 8, 8, 64, 0.1, 0, A, big, None) == 5
@@ -191,16 +191,14 @@ def test_dropout_rejects_before_touching_the_device():
     g = fa.lib().fa2_bwd_dropout
     big = 1 << 30
     assert g(None, *([A] * 8), 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, A, big, None) == 1
-    assert g(*([A] * 9), 1, 1, 8, 8, 256, 0.1, 1, 0.1, 1, 0, A, big, None) == 3
+    assert g(*([A] * 9), 1, 1, 8, 8, 80, 0.1, 1, 0.1, 1, 0, A, big, None) == 3
     assert g(*([A] * 9), 1, 1, 8, 8, 64, 0.1, 1, 1.0, 1, 0, A, big, None) == 4
     assert g(*([A] * 9), 1, 1, 8, 8, 64, 0.1, 1, 0.1, 1, 0, A, 4, None) == 8
 
 
-def test_head_dim_256_only_for_16bit_forward():
+def test_head_dims_96_and_256_only_for_16bit_data():
+    # (no call here may pass every check: it would launch on the stand-in pointers)
     L = fa.lib()
-    big = 1 << 30
-    args = [A] * 9
-    assert L.fa2_bwd(*args, 1, 1, 8, 8, 256, 0.1, 0, A, big, None) == 3
     assert L.fa2_fwd_f32(A, A, A, A, A, 1, 1, 8, 8, 96, 0.1, 0, None) == 3
     assert L.fa2_fwd_f32(A, A, A, A, A, 1, 1, 8, 8, 256, 0.1, 0, None) == 3
     assert fa.fa2_splitkv_workspace_bytes(1, 1, 8, 8, 256, 0, 2) > 0

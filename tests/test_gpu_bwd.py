@@ -63,6 +63,9 @@ SHAPES = [
     (1, 2, 129, 129, 96),
     (2, 1, 300, 511, 96),
     (1, 1, 1, 300, 96),
+    (1, 2, 129, 129, 256),
+    (1, 1, 300, 200, 256),
+    (2, 1, 65, 333, 256),
 ]
 
 
@@ -122,6 +125,24 @@ def test_bwd_parity_d96_long():
                                      rows=rows, keys=keys)
         got = (dq[b, h, rows][None, None], dk[b, h, keys][None, None], dv[b, h, keys][None, None])
         compare_grads("d96 long head (%d,%d)" % (b, h), got, want)
+
+
+def test_bwd_parity_d256_long():
+    """d = 256 at N=2048 (B=1, H=8, causal); 2 heads, 256 sampled rows and keys each."""
+    B, H, L, d = 1, 8, 2048, 256
+    q, k, v = random_qkv(B, H, L, L, d, "bf16", seed=2561)
+    do = random_dout(B, H, L, d, "bf16", seed=2561)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    say("case d256 long (bwd)")
+    dq, dk, dv = gpu_grads(q, k, v, do, True, scale)
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        rows = sample_rows(L, 256, 2562 + b * H + h)
+        keys = sample_rows(L, 256, 2563 + b * H + h)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        want = ref.attention_bwd_f64(widen(q[sl]), widen(k[sl]), widen(v[sl]), widen(do[sl]), scale, True,
+                                     rows=rows, keys=keys)
+        got = (dq[b, h, rows][None, None], dk[b, h, keys][None, None], dv[b, h, keys][None, None])
+        compare_grads("d256 long head (%d,%d)" % (b, h), got, want)
 
 
 def test_bwd_closed_forms():

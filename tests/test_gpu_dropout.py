@@ -178,6 +178,7 @@ BWD_CASES = [
     (1, 1, 640, 640, 128, True, 0.3),
     (1, 1, 333, 129, 64, True, 0.6),
     (1, 2, 300, 257, 96, False, 0.25),
+    (1, 1, 200, 300, 256, True, 0.2),
 ]
 
 
@@ -201,7 +202,7 @@ def test_dropout_backward_zero_rate_is_plain_backward():
 
 
 @pytest.mark.parametrize("d,Lq,causal", [(128, 128, False), (128, 100, True), (64, 64, False), (32, 32, True),
-                                         (96, 96, False)])
+                                         (96, 96, False), (256, 200, True)])
 def test_dropout_backward_mask_exact(d, Lq, causal):
     """dout = I (Lq <= d): dv[j, i] = (256 / t) P[i, j] Z[i, j], so the nonzero
     pattern of dv[..., :Lq] is the transposed keep mask (and the causal mask) bit

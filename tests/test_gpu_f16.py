@@ -63,7 +63,7 @@ def test_f16_forward_headline_shape_sampled():
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(1, 2, 129, 129, 64), (2, 1, 257, 255, 128), (1, 1, 500, 300, 128),
-                                   (1, 2, 200, 333, 96)],
+                                   (1, 2, 200, 333, 96), (1, 1, 150, 270, 256)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_f16_backward_parity(shape, causal):
     B, H, Lq, Lk, d = shape

@@ -96,6 +96,7 @@ BWD_CASES = [
     (1, 1, 640, 640, 64, 127, -1),
     (1, 2, 300, 300, 32, 20, 3),
     (1, 2, 300, 400, 96, 50, 0),
+    (1, 1, 300, 400, 256, 70, 10),
 ]
 
 
