@@ -21,6 +21,10 @@ constexpr int kWorkgroupsPerCU = 2;
 // Fewest K/V tiles a split-KV range should have, so the partial kernel's
 // software pipeline and double buffering have something to overlap.
 constexpr int kMinTilesPerSplit = 8;
+// The decoding kernel (Lq <= 4): work-groups per CU the automatic split count
+// aims for, and the fewest keys per range.
+constexpr int kDecodeWorkgroupsPerCU = 2;
+constexpr int kMinDecodeKeys = 256;
 
 int check_device()
 {
@@ -129,16 +133,25 @@ int dropout_setup(double p_drop, uint64_t seed, uint32_t offset, fa2::DropoutPar
     return FA2_OK;
 }
 
-// Split count for num_splits == 0: the fewest ranges that put one work-group
-// on every compute unit, or two under the causal mask (query tiles then differ
-// in length, and finer pieces even out the end of the launch).  Measured on
-// MI355X, more splits than that cost more in partial-result traffic and per
-// work-group start-up than they gain.  Every range keeps at least
-// kMinTilesPerSplit K/V tiles.
+// Split count for num_splits == 0 (Lq <= 4: the decoding kernel's rule below):
+// the fewest ranges that put one work-group on every compute unit, or two under
+// the causal mask (query tiles then differ in length, and finer pieces even out
+// the end of the launch).  Measured on MI355X, more splits than that cost more in
+// partial-result traffic and per work-group start-up than they gain.  Every range
+// keeps at least kMinTilesPerSplit K/V tiles.
 int auto_splits(int B, int H, int Lq, int Lk, int causal)
 {
     const int cus = device_cus();
     if (cus <= 0) return 1;
+    if (Lq <= fa2::kDecodeMaxRows) {
+        // Decoding kernel: two work-groups per CU keep enough loads in flight;
+        // every range keeps at least kMinDecodeKeys keys.
+        const int64_t keys = causal ? (Lq < Lk ? Lq : Lk) : Lk;
+        int64_t S = ((int64_t)kDecodeWorkgroupsPerCU * cus + (int64_t)B * H - 1) / ((int64_t)B * H);
+        if (S > keys / kMinDecodeKeys) S = keys / kMinDecodeKeys;
+        if (S > FA2_MAX_SPLITS) S = FA2_MAX_SPLITS;
+        return S < 1 ? 1 : (int)S;
+    }
     const int64_t target = (int64_t)cus * (causal ? kWorkgroupsPerCU : 1);
     const int64_t n_qtiles = (Lq + fa2::kBr - 1) / fa2::kBr;
     const int64_t base = n_qtiles * B * H;
@@ -351,8 +364,13 @@ int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float 
     pp.o = o_parts;
     pp.lse = lse_parts;
     pp.n_splits = S;
-    pp.n_wg = p.n_wg * S;
-    if (fa2::launch_fwd_bf16_split(pp, d, causal != 0, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    if (Lq <= fa2::kDecodeMaxRows) {          // a few query rows: the decoding kernel
+        pp.n_wg = B * H * S;
+        if (fa2::launch_decode(pp, d, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    } else {
+        pp.n_wg = p.n_wg * S;
+        if (fa2::launch_fwd_bf16_split(pp, d, causal != 0, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    }
     if (fa2::launch_merge(o_parts, lse_parts, S, rows, d, o, lse, s) != hipSuccess) return FA2_ERR_LAUNCH;
     return FA2_OK;
 }

@@ -147,4 +147,8 @@ hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float 
 hipError_t launch_bwd_bf16_dropout(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                         int d, void *o, float *lse, hipStream_t stream);
+// Split-KV partials for Lq <= kDecodeMaxRows (bf16), same outputs as
+// launch_fwd_bf16_split; p.n_wg = B * H * p.n_splits.
+constexpr int kDecodeMaxRows = 4;
+hipError_t launch_decode(const FwdParams &p, int d, hipStream_t stream);
 }  // namespace fa2

@@ -162,6 +162,11 @@ int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float 
  *  2. A merge kernel (fa2_merge_partials below) combines the partials of every
  *     row.
  *
+ * With Lq <= 4 (decoding) stage 1 runs a kernel for a few query rows instead: one
+ * work-group per (b, h, range) streams the range's K and V rows into registers and
+ * takes the dot products and the weighted sum of V on the vector ALU in fp32 (the
+ * probabilities are not rounded to bf16 there); the partials have the same form.
+ *
  * Arguments as fa2_fwd, plus
  *   num_splits     : number of K/V ranges, 1..FA2_MAX_SPLITS; 0 picks a count
  *                    for the current device (fa2_splitkv_num_splits).  Ranges of
@@ -196,7 +201,9 @@ size_t fa2_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int caus
  * compute unit of the current device one (Q block, range) work-group, or two
  * when causal (Q blocks then differ in length), with at least 8 K/V blocks per
  * range and at most FA2_MAX_SPLITS ranges; 1 when the Q blocks alone fill the
- * device.  Returns 1 if the device cannot be queried.
+ * device.  With Lq <= 4: the fewest ranges that give every compute unit two
+ * (b, h, range) work-groups, with at least 256 keys per range.  Returns 1 if the
+ * device cannot be queried.
  */
 int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal);
 

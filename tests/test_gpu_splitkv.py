@@ -49,6 +49,33 @@ def test_splitkv_ragged(shape, causal, splits):
                num_splits=splits)
 
 
+DECODE_SHAPES = [
+    # B, H, Lq, Lk, d   (Lq <= 4: the split-KV path runs the decoding kernel)
+    (1, 4, 1, 4097, 128),
+    (2, 3, 2, 1000, 64),
+    (1, 2, 3, 777, 96),
+    (1, 2, 4, 2048, 256),
+    (3, 1, 4, 100, 32),
+    (1, 1, 1, 5, 128),      # more splits than keys: most ranges empty
+    (2, 2, 3, 3, 64),
+]
+
+
+@pytest.mark.parametrize("splits", [2, 7, 0])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_kernel_parity(shape, causal, splits):
+    B, H, Lq, Lk, d = shape
+    q, k, v = random_qkv(B, H, Lq, Lk, d, "bf16", seed=sum(shape) + 3 * causal + splits)
+    check_case("decode %s S=%d" % (shape, splits), q, k, v, causal, _scale(d), "bf16", num_splits=splits)
+
+
+def test_decode_kernel_peaky_scores():
+    """Q x 8 (scores spread over tens of units): the per-step max moves often."""
+    q, k, v = random_qkv(1, 2, 2, 3000, 128, "bf16", seed=77, q_mult=8.0)
+    check_case("decode peaky", q, k, v, False, _scale(128), "bf16", num_splits=0)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_splitkv_more_splits_than_tiles(causal):
     """S = 128 on 5 K/V tiles: most ranges are empty, and (causal) most rows of a
