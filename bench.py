@@ -174,8 +174,8 @@ def main():
     w = dict(WORKLOADS, **DECODE_WORKLOADS)[args.workload or HEADLINE]
     if args.fp16:
         import dataclasses
-        if w.dtype != "bf16" or args.splits is not None or args.window is not None:
-            print("bench.py: --fp16 takes a bf16 workload, without --splits or --window", file=sys.stderr)
+        if w.dtype != "bf16":
+            print("bench.py: --fp16 takes a bf16 workload", file=sys.stderr)
             sys.exit(2)
         w = dataclasses.replace(w, dtype="fp16")
     q, k, v = workload_inputs(w)
@@ -184,22 +184,24 @@ def main():
     lse = torch.empty((w.B, w.H, w.Lq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     args_common = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal))
+    # the fp16 twin of a 16-bit entry point
+    f16 = (lambda name: getattr(fa, name + "_f16")) if w.dtype == "fp16" else (lambda name: getattr(fa, name))
     split_info = None
     bwd_info = None
     win_info = None
     flops_override = None
     drop_info = None
     if args.dropout is not None:
-        if w.dtype != "bf16" or args.splits is not None or args.window is not None or args.fp16:
-            print("bench.py: --dropout takes a bf16 workload, without --splits, --window or --fp16",
+        if w.dtype not in ("bf16", "fp16") or args.splits is not None or args.window is not None:
+            print("bench.py: --dropout takes a bf16 (or --fp16) workload, without --splits or --window",
                   file=sys.stderr)
             sys.exit(2)
         drop_args = (float(args.dropout), 0x5EED, 0)
         drop_info = {"p": float(args.dropout), "seed": 0x5EED, "offset": 0,
                      "flops_count": "as without dropout (the mask adds no matrix work)"}
     if args.window is not None:
-        if w.dtype != "bf16" or args.splits is not None or args.backward:
-            print("bench.py: --window takes a bf16 workload, without --splits or --backward",
+        if w.dtype not in ("bf16", "fp16") or args.splits is not None or args.backward:
+            print("bench.py: --window takes a bf16 (or --fp16) workload, without --splits or --backward",
                   file=sys.stderr)
             sys.exit(2)
         import numpy as np
@@ -209,7 +211,7 @@ def main():
         hi = np.minimum(w.Lk, i + wr + 1) if wr >= 0 else np.full_like(i, w.Lk)
         pairs = int(np.maximum(hi - lo, 0).sum())
         flops_override = 4.0 * w.B * w.H * w.d * pairs
-        fn = fa.fa2_fwd_window
+        fn = f16("fa2_fwd_window")
         call = (dq, dk, dv, o, lse, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, wl, wr, stream.cuda_stream)
         win_info = {"window_left": wl, "window_right": wr, "visible_pairs_per_head": pairs,
                     "flops_count": "4*d per visible (query, key) pair"}
@@ -221,7 +223,7 @@ def main():
         do = random_dout(w.B, w.H, w.Lq, w.d, w.dtype, seed=w.seed)
         ddo = do.cuda()
         if drop_info is not None:
-            fa.fa2_fwd_dropout(*(args_common + drop_args + (stream.cuda_stream,)))
+            f16("fa2_fwd_dropout")(*(args_common + drop_args + (stream.cuda_stream,)))
         else:
             (fa.fa2_fwd_f16 if w.dtype == "fp16" else fa.fa2_fwd)(*(args_common + (stream.cuda_stream,)))
         gq, gk, gv = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
@@ -231,25 +233,25 @@ def main():
         call = (dq, dk, dv, o, lse, ddo, gq, gk, gv, w.B, w.H, w.Lq, w.Lk, w.d, w.scale, int(w.causal),
                 workspace, ws_bytes, stream.cuda_stream)
         if drop_info is not None:
-            fn = fa.fa2_bwd_dropout
+            fn = f16("fa2_bwd_dropout")
             call = call[:16] + drop_args + call[16:]
         bwd_info = {"timed_call": "fa2_bwd = prep + dK/dV + dQ kernels", "workspace_bytes": ws_bytes,
                     "flops_count": "2.5x forward (S, dP, dV, dK, dQ); the dQ pass recomputes S and dP, "
                                    "so the device executes 3.5x"}
     elif drop_info is not None:
-        fn = fa.fa2_fwd_dropout
+        fn = f16("fa2_fwd_dropout")
         call = args_common + drop_args + (stream.cuda_stream,)
     elif args.splits is None:
         fn = {"bf16": fa.fa2_fwd, "fp16": fa.fa2_fwd_f16, "fp32": fa.fa2_fwd_f32}[w.dtype]
         call = args_common + (stream.cuda_stream,)
     else:
-        if w.dtype != "bf16":
-            print("bench.py: the split-KV path takes bf16 workloads", file=sys.stderr)
+        if w.dtype not in ("bf16", "fp16"):
+            print("bench.py: the split-KV path takes bf16 (or --fp16) workloads", file=sys.stderr)
             sys.exit(2)
         S = args.splits or fa.fa2_splitkv_num_splits(w.B, w.H, w.Lq, w.Lk, w.d, int(w.causal))
         ws_bytes = fa.fa2_splitkv_workspace_bytes(w.B, w.H, w.Lq, w.Lk, w.d, int(w.causal), S)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-        fn = fa.fa2_fwd_splitkv
+        fn = f16("fa2_fwd_splitkv")
         call = args_common + (S, workspace, ws_bytes, stream.cuda_stream)
         split_info = {"num_splits": S, "requested": args.splits, "workspace_bytes": ws_bytes,
                       "timed_call": "fa2_fwd_splitkv = partial kernel + merge kernel"}

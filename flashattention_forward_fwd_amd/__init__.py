@@ -10,16 +10,23 @@ and the stream.
 """
 import math
 
-from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_dropout, fa2_bwd_f16, fa2_bwd_window,  # noqa: F401
-                   fa2_bwd_workspace_bytes,
-                   fa2_check_args, fa2_fwd, fa2_fwd_f16, fa2_fwd_f32, fa2_fwd_splitkv, fa2_fwd_window,
-                   fa2_fwd_dropout, fa2_merge_partials,
-                   fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib, status_string)
+from . import _lib
+from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_dropout, fa2_bwd_dropout_f16,  # noqa: F401
+                   fa2_bwd_f16, fa2_bwd_window, fa2_bwd_window_f16, fa2_bwd_workspace_bytes, fa2_check_args,
+                   fa2_fwd, fa2_fwd_dropout, fa2_fwd_dropout_f16, fa2_fwd_f16, fa2_fwd_f32, fa2_fwd_splitkv,
+                   fa2_fwd_splitkv_f16, fa2_fwd_window, fa2_fwd_window_f16, fa2_merge_partials,
+                   fa2_merge_partials_f16, fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib,
+                   status_string)
 
-__all__ = ["forward", "backward", "merge_partials", "fa2_fwd", "fa2_fwd_f16", "fa2_fwd_f32", "fa2_fwd_splitkv",
-           "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_merge_partials",
-           "fa2_fwd_window", "fa2_fwd_dropout", "fa2_bwd", "fa2_bwd_f16", "fa2_bwd_window", "fa2_bwd_dropout", "fa2_bwd_workspace_bytes", "fa2_check_args", "FA2Error", "status_string",
-           "FA2_MAX_SPLITS"]
+__all__ = ["forward", "backward", "merge_partials", "FA2Error", "status_string", "FA2_MAX_SPLITS",
+           "fa2_check_args", "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_bwd_workspace_bytes"] + \
+    sorted(n for n in _lib.SIGNATURES if n.startswith("fa2_") and n not in ("fa2_status_string",))
+
+
+def _entry(name, dtype):
+    """The bf16 entry point `name` or its fp16 twin for torch dtype `dtype`."""
+    import torch
+    return getattr(_lib, name + ("_f16" if dtype == torch.float16 else ""))
 
 
 def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=None, workspace=None,
@@ -30,19 +37,21 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
     (made contiguous).  scale defaults to fp32(1/sqrt(d)).  Returns (o, lse)
     with o like q and lse fp32 [B, H, Lq].  Enqueued on the current stream.
 
-    num_splits (bf16 only): None runs the one-pass kernel; an int runs the
+    num_splits (16-bit only): None runs the one-pass kernel; an int runs the
     split-KV path with that many K/V ranges (0: the library picks).  Its
     workspace is allocated here unless a large enough uint8 device tensor is
     given.
 
-    window (bf16 only): (window_left, window_right) runs ``fa2_fwd_window`` --
+    window (16-bit only): (window_left, window_right) runs ``fa2_fwd_window`` --
     key j visible to query i iff i - window_left <= j <= i + window_right, a
     negative bound meaning unbounded; causal must then be False.
 
-    dropout (bf16 only): (p, seed, offset) runs ``fa2_fwd_dropout`` -- each
+    dropout (16-bit only): (p, seed, offset) runs ``fa2_fwd_dropout`` -- each
     probability kept with probability round(256 (1 - p)) / 256 by the Philox
     keep mask of (seed, offset), kept ones scaled up by the inverse; lse is the
     one without dropout.  Pass the same tuple to ``backward``.
+
+    The fp16 twins (``*_f16``) run for float16 tensors.
     """
     import torch
 
@@ -65,41 +74,42 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     c = int(bool(causal))
+    if (dropout is not None or window is not None or num_splits is not None) and q.dtype == torch.float32:
+        raise ValueError("dropout, window and num_splits take bfloat16 or float16 tensors")
     if dropout is not None:
-        if q.dtype != torch.bfloat16 or window is not None or num_splits is not None:
-            raise ValueError("dropout takes bfloat16 tensors, no window and no num_splits")
+        if window is not None or num_splits is not None:
+            raise ValueError("dropout takes no window and no num_splits")
         p_drop, seed, offset = dropout
-        fa2_fwd_dropout(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, float(p_drop), int(seed), int(offset),
-                        stream)
+        _entry("fa2_fwd_dropout", q.dtype)(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, float(p_drop), int(seed),
+                                           int(offset), stream)
         return out, lse
     if window is not None:
-        if q.dtype != torch.bfloat16 or causal or num_splits is not None:
-            raise ValueError("window takes bfloat16 tensors, causal=False and no num_splits")
+        if causal or num_splits is not None:
+            raise ValueError("window replaces the causal mask (causal=False) and takes no num_splits")
         wl, wr = window
-        fa2_fwd_window(q, k, v, out, lse, B, H, Lq, Lk, d, scale, int(wl), int(wr), stream)
+        _entry("fa2_fwd_window", q.dtype)(q, k, v, out, lse, B, H, Lq, Lk, d, scale, int(wl), int(wr), stream)
         return out, lse
     if num_splits is not None:
-        if q.dtype != torch.bfloat16:
-            raise ValueError("the split-KV path takes bfloat16 tensors")
         need = fa2_splitkv_workspace_bytes(B, H, Lq, Lk, d, c, num_splits)
         if need == 0:
             raise ValueError("sizes or num_splits rejected by fa2_splitkv_workspace_bytes")
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        fa2_fwd_splitkv(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, num_splits, workspace,
-                        workspace.numel() * workspace.element_size(), stream)
+        _entry("fa2_fwd_splitkv", q.dtype)(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, num_splits, workspace,
+                                           workspace.numel() * workspace.element_size(), stream)
         return out, lse
     fn = {torch.bfloat16: fa2_fwd, torch.float16: fa2_fwd_f16, torch.float32: fa2_fwd_f32}[q.dtype]
     fn(q, k, v, out, lse, B, H, Lq, Lk, d, scale, c, stream)
     return out, lse
 
 
-def merge_partials(o_parts, lse_parts, out=None, lse=None):
+def merge_partials(o_parts, lse_parts, out=None, lse=None, dtype=None):
     """Combine partial results over disjoint key sets (libfa2 ``fa2_merge_partials``).
 
     o_parts: fp32 [S, ..., d], lse_parts: fp32 [S, ...] (natural-log
     logsumexps, -inf for an empty part) on the device.  Returns (o, lse) with
-    o bf16 [..., d] and lse fp32 [...].  Enqueued on the current stream.
+    o [..., d] in dtype (bfloat16 by default, or float16, or out's dtype) and lse
+    fp32 [...].  Enqueued on the current stream.
     """
     import torch
 
@@ -112,12 +122,16 @@ def merge_partials(o_parts, lse_parts, out=None, lse=None):
     S, d = o_parts.shape[0], o_parts.shape[-1]
     rows = lse_parts[0].numel()
     o_parts, lse_parts = o_parts.contiguous(), lse_parts.contiguous()
+    if dtype is None:
+        dtype = out.dtype if out is not None else torch.bfloat16
+    if dtype not in (torch.bfloat16, torch.float16) or (out is not None and out.dtype != dtype):
+        raise ValueError("the merged output is bfloat16 or float16")
     if out is None:
-        out = torch.empty(o_parts.shape[1:], dtype=torch.bfloat16, device=o_parts.device)
+        out = torch.empty(o_parts.shape[1:], dtype=dtype, device=o_parts.device)
     if lse is None:
         lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device)
     stream = torch.cuda.current_stream(o_parts.device).cuda_stream
-    fa2_merge_partials(o_parts, lse_parts, S, rows, d, out, lse, stream)
+    _entry("fa2_merge_partials", dtype)(o_parts, lse_parts, S, rows, d, out, lse, stream)
     return out, lse
 
 
@@ -127,12 +141,13 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
 
     q, k, v, o, dout: bfloat16 (or all float16) CUDA tensors (q, o, dout [B, H, Lq, d]; k, v
     [B, H, Lk, d]), o and lse (fp32 [B, H, Lq]) as returned by ``forward`` for
-    the same q, k, v, causal and scale.  Returns bf16 (dq, dk, dv).  The
+    the same q, k, v, causal and scale.  Returns (dq, dk, dv) in q's dtype.  The
     workspace is allocated here unless a large enough uint8 device tensor is
     given.  window: (window_left, window_right) of a ``forward(..., window=...)``
     call runs ``fa2_bwd_window`` (causal must then be False).  dropout: the
     (p, seed, offset) of a ``forward(..., dropout=...)`` call runs
-    ``fa2_bwd_dropout`` (bf16).  Enqueued on the current stream.
+    ``fa2_bwd_dropout``.  float16 tensors run the ``*_f16`` twins.  Enqueued on
+    the current stream.
     """
     import torch
 
@@ -164,18 +179,19 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
     stream = torch.cuda.current_stream(q.device).cuda_stream
     nbytes = workspace.numel() * workspace.element_size()
     if dropout is not None:
-        if window is not None or q.dtype != torch.bfloat16:
-            raise ValueError("dropout takes bfloat16 tensors and no window")
+        if window is not None:
+            raise ValueError("dropout takes no window")
         p_drop, seed, offset = dropout
-        fa2_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), float(p_drop),
-                        int(seed), int(offset), workspace, nbytes, stream)
+        _entry("fa2_bwd_dropout", q.dtype)(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale,
+                                           int(bool(causal)), float(p_drop), int(seed), int(offset), workspace,
+                                           nbytes, stream)
         return dq, dk, dv
     if window is not None:
-        if causal or q.dtype != torch.bfloat16:
-            raise ValueError("window takes bfloat16 tensors and replaces the causal mask (causal=False)")
-        fa2_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(window[0]), int(window[1]),
-                       workspace, nbytes, stream)
+        if causal:
+            raise ValueError("window replaces the causal mask (causal=False)")
+        _entry("fa2_bwd_window", q.dtype)(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale,
+                                          int(window[0]), int(window[1]), workspace, nbytes, stream)
         return dq, dk, dv
-    fn = fa2_bwd if q.dtype == torch.bfloat16 else fa2_bwd_f16
-    fn(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)), workspace, nbytes, stream)
+    _entry("fa2_bwd", q.dtype)(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, int(bool(causal)),
+                               workspace, nbytes, stream)
     return dq, dk, dv

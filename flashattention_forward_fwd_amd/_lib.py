@@ -45,6 +45,10 @@ SIGNATURES = {
     "fa2_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _D, _U64, _U32, _P, _Z,
                              _P]),
 }
+# fp16 twins: the same arguments
+for _n in ("fa2_fwd_window", "fa2_fwd_dropout", "fa2_fwd_splitkv", "fa2_merge_partials", "fa2_bwd_window",
+           "fa2_bwd_dropout"):
+    SIGNATURES[_n + "_f16"] = SIGNATURES[_n]
 
 _lib = None
 
@@ -76,138 +80,140 @@ def status_string(status):
     return lib().fa2_status_string(int(status)).decode()
 
 
-def _ptr(x):
-    """Device address of a tensor (data_ptr) or a raw integer address."""
-    if x is None:
-        return None
+def _arg(x):
+    """A tensor becomes its device address (data_ptr); everything else passes as is
+    (ctypes converts it by the declared argument type)."""
     if hasattr(x, "data_ptr"):
         return x.data_ptr()
-    return int(x)
+    return x
 
 
+def _call(name, *args):
+    """Call the libfa2 entry point `name`; raise FA2Error on a non-OK status."""
+    st = getattr(lib(), name)(*(_arg(a) for a in args))
+    if st != FA2_OK:
+        raise FA2Error(st, name)
+
+
+# Entry points that return an fa2_status: tensors or raw device addresses; raise FA2Error.
 def fa2_fwd(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
-    """libfa2 ``fa2_fwd`` (bf16).  Tensors or raw device addresses; raises FA2Error."""
-    st = lib().fa2_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                       int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                       _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_fwd")
-
-
-def fa2_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
-    """libfa2 ``fa2_fwd_f32``.  Tensors or raw device addresses; raises FA2Error."""
-    st = lib().fa2_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                           int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                           _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_fwd_f32")
+    """``fa2_fwd`` (bf16)."""
+    _call("fa2_fwd", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream)
 
 
 def fa2_fwd_f16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
-    """libfa2 ``fa2_fwd_f16``.  Tensors or raw device addresses; raises FA2Error."""
-    st = lib().fa2_fwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                           int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                           _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_fwd_f16")
+    """``fa2_fwd_f16`` (fp16)."""
+    _call("fa2_fwd_f16", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream)
 
 
-def fa2_check_args(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes):
-    """libfa2 ``fa2_check_args``: the status the entry points would return (no HIP call)."""
-    return lib().fa2_check_args(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                int(B), int(H), int(Lq), int(Lk), int(d), float(scale),
-                                int(causal), int(elem_bytes))
-
-
-def fa2_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
-                    workspace_bytes, stream):
-    """libfa2 ``fa2_fwd_splitkv`` (bf16, split K/V + merge).  Raises FA2Error."""
-    st = lib().fa2_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                               int(num_splits), _ptr(workspace), int(workspace_bytes), _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_fwd_splitkv")
-
-
-def fa2_splitkv_workspace_bytes(B, H, Lq, Lk, d, causal, num_splits):
-    """libfa2 ``fa2_splitkv_workspace_bytes``: bytes of workspace (0: sizes rejected)."""
-    return lib().fa2_splitkv_workspace_bytes(int(B), int(H), int(Lq), int(Lk), int(d), int(causal),
-                                             int(num_splits))
-
-
-def fa2_splitkv_num_splits(B, H, Lq, Lk, d, causal):
-    """libfa2 ``fa2_splitkv_num_splits``: the split count that num_splits=0 selects."""
-    return lib().fa2_splitkv_num_splits(int(B), int(H), int(Lq), int(Lk), int(d), int(causal))
-
-
-def fa2_merge_partials(o_parts, lse_parts, n_parts, rows, d, o, lse, stream):
-    """libfa2 ``fa2_merge_partials``.  Raises FA2Error."""
-    st = lib().fa2_merge_partials(_ptr(o_parts), _ptr(lse_parts), int(n_parts), int(rows), int(d),
-                                  _ptr(o), _ptr(lse), _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_merge_partials")
-
-
-def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
-            workspace_bytes, stream):
-    """libfa2 ``fa2_bwd`` (bf16 gradients dq, dk, dv).  Raises FA2Error."""
-    st = lib().fa2_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                       _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                       _ptr(workspace), int(workspace_bytes), _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_bwd")
-
-
-def fa2_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
-                workspace_bytes, stream):
-    """libfa2 ``fa2_bwd_f16`` (fp16 gradients).  Raises FA2Error."""
-    st = lib().fa2_bwd_f16(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                           _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                           _ptr(workspace), int(workspace_bytes), _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_bwd_f16")
-
-
-def fa2_bwd_workspace_bytes(B, H, Lq):
-    """libfa2 ``fa2_bwd_workspace_bytes``: bytes of backward workspace (0: sizes rejected)."""
-    return lib().fa2_bwd_workspace_bytes(int(B), int(H), int(Lq))
+def fa2_fwd_f32(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream):
+    """``fa2_fwd_f32`` (fp32)."""
+    _call("fa2_fwd_f32", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, stream)
 
 
 def fa2_fwd_window(q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_right, stream):
-    """libfa2 ``fa2_fwd_window`` (bf16, keys i - window_left .. i + window_right).  Raises FA2Error."""
-    st = lib().fa2_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                              int(B), int(H), int(Lq), int(Lk), int(d), float(scale),
-                              int(window_left), int(window_right), _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_fwd_window")
+    """``fa2_fwd_window`` (bf16, keys i - window_left .. i + window_right)."""
+    _call("fa2_fwd_window", q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_right, stream)
+
+
+def fa2_fwd_window_f16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_right, stream):
+    """``fa2_fwd_window_f16`` (fp16)."""
+    _call("fa2_fwd_window_f16", q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_right, stream)
 
 
 def fa2_fwd_dropout(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset, stream):
-    """libfa2 ``fa2_fwd_dropout`` (bf16, Philox keep mask of (seed, offset)).  Raises FA2Error."""
-    st = lib().fa2_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                               int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                               float(dropout_p), int(seed), int(offset), _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_fwd_dropout")
+    """``fa2_fwd_dropout`` (bf16, Philox keep mask of (seed, offset))."""
+    _call("fa2_fwd_dropout", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset, stream)
 
 
-def fa2_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset,
-                    workspace, workspace_bytes, stream):
-    """libfa2 ``fa2_bwd_dropout`` (gradients of fa2_fwd_dropout).  Raises FA2Error."""
-    st = lib().fa2_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                               _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale), int(causal),
-                               float(dropout_p), int(seed), int(offset), _ptr(workspace), int(workspace_bytes),
-                               _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_bwd_dropout")
+def fa2_fwd_dropout_f16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset, stream):
+    """``fa2_fwd_dropout_f16`` (fp16)."""
+    _call("fa2_fwd_dropout_f16", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset,
+          stream)
+
+
+def fa2_fwd_splitkv(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace, workspace_bytes,
+                    stream):
+    """``fa2_fwd_splitkv`` (bf16, split K/V + merge)."""
+    _call("fa2_fwd_splitkv", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
+          workspace_bytes, stream)
+
+
+def fa2_fwd_splitkv_f16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
+                        workspace_bytes, stream):
+    """``fa2_fwd_splitkv_f16`` (fp16)."""
+    _call("fa2_fwd_splitkv_f16", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
+          workspace_bytes, stream)
+
+
+def fa2_merge_partials(o_parts, lse_parts, n_parts, rows, d, o, lse, stream):
+    """``fa2_merge_partials`` (bf16 output)."""
+    _call("fa2_merge_partials", o_parts, lse_parts, n_parts, rows, d, o, lse, stream)
+
+
+def fa2_merge_partials_f16(o_parts, lse_parts, n_parts, rows, d, o, lse, stream):
+    """``fa2_merge_partials_f16`` (fp16 output)."""
+    _call("fa2_merge_partials_f16", o_parts, lse_parts, n_parts, rows, d, o, lse, stream)
+
+
+def fa2_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace, workspace_bytes,
+            stream):
+    """``fa2_bwd`` (bf16 gradients dq, dk, dv)."""
+    _call("fa2_bwd", q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+          workspace_bytes, stream)
+
+
+def fa2_bwd_f16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace, workspace_bytes,
+                stream):
+    """``fa2_bwd_f16`` (fp16 gradients)."""
+    _call("fa2_bwd_f16", q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+          workspace_bytes, stream)
 
 
 def fa2_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, window_left, window_right,
                    workspace, workspace_bytes, stream):
-    """libfa2 ``fa2_bwd_window`` (gradients of fa2_fwd_window).  Raises FA2Error."""
-    st = lib().fa2_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
-                              _ptr(dv), int(B), int(H), int(Lq), int(Lk), int(d), float(scale),
-                              int(window_left), int(window_right), _ptr(workspace), int(workspace_bytes),
-                              _ptr(stream))
-    if st != FA2_OK:
-        raise FA2Error(st, "fa2_bwd_window")
+    """``fa2_bwd_window`` (gradients of fa2_fwd_window)."""
+    _call("fa2_bwd_window", q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, window_left,
+          window_right, workspace, workspace_bytes, stream)
+
+
+def fa2_bwd_window_f16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, window_left, window_right,
+                       workspace, workspace_bytes, stream):
+    """``fa2_bwd_window_f16`` (gradients of fa2_fwd_window_f16)."""
+    _call("fa2_bwd_window_f16", q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, window_left,
+          window_right, workspace, workspace_bytes, stream)
+
+
+def fa2_bwd_dropout(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset,
+                    workspace, workspace_bytes, stream):
+    """``fa2_bwd_dropout`` (gradients of fa2_fwd_dropout)."""
+    _call("fa2_bwd_dropout", q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, dropout_p, seed,
+          offset, workspace, workspace_bytes, stream)
+
+
+def fa2_bwd_dropout_f16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, dropout_p, seed,
+                        offset, workspace, workspace_bytes, stream):
+    """``fa2_bwd_dropout_f16`` (gradients of fa2_fwd_dropout_f16)."""
+    _call("fa2_bwd_dropout_f16", q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, dropout_p,
+          seed, offset, workspace, workspace_bytes, stream)
+
+
+# Size and query helpers (no status).
+def fa2_check_args(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes):
+    """``fa2_check_args``: the status the entry points would return (no HIP call)."""
+    return lib().fa2_check_args(*(_arg(a) for a in (q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, elem_bytes)))
+
+
+def fa2_splitkv_workspace_bytes(B, H, Lq, Lk, d, causal, num_splits):
+    """``fa2_splitkv_workspace_bytes``: bytes of workspace (0: sizes rejected)."""
+    return lib().fa2_splitkv_workspace_bytes(B, H, Lq, Lk, d, causal, num_splits)
+
+
+def fa2_splitkv_num_splits(B, H, Lq, Lk, d, causal):
+    """``fa2_splitkv_num_splits``: the split count that num_splits=0 selects."""
+    return lib().fa2_splitkv_num_splits(B, H, Lq, Lk, d, causal)
+
+
+def fa2_bwd_workspace_bytes(B, H, Lq):
+    """``fa2_bwd_workspace_bytes``: bytes of backward workspace (0: sizes rejected)."""
+    return lib().fa2_bwd_workspace_bytes(B, H, Lq)

@@ -239,6 +239,143 @@ int prepare_bwd(const void *q, const void *k, const void *v, const void *o, cons
     return FA2_OK;
 }
 
+// ---- the 16-bit entry points, shared by the bf16 and fp16 (f16) names
+
+int fwd16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Lq, int Lk, int d,
+          float scale, int causal, bool f16, void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
+    if (st != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (fa2::launch_fwd16(p, d, causal != 0, f16, fa2::FwdVariant::kPlain, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fwd_window16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Lq, int Lk,
+                 int d, float scale, int window_left, int window_right, bool f16, void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 2, &p, kDims16);
+    if (st != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    // Negative bounds all mean "unbounded"; keep them as -1.
+    p.wl = window_left < 0 ? -1 : window_left;
+    p.wr = window_right < 0 ? -1 : window_right;
+    if (fa2::launch_fwd16(p, d, false, f16, fa2::FwdVariant::kWindow, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fwd_dropout16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Lq, int Lk,
+                  int d, float scale, int causal, double dropout_p, uint64_t seed, uint32_t offset, bool f16,
+                  void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
+    if (st != FA2_OK) return st;
+    if ((st = dropout_setup(dropout_p, seed, offset, &p.drop)) != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (fa2::launch_fwd16(p, d, causal != 0, f16, fa2::FwdVariant::kDropout, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int fwd_splitkv16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Lq, int Lk,
+                  int d, float scale, int causal, int num_splits, void *workspace, size_t workspace_bytes_given,
+                  bool f16, void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
+    if (st != FA2_OK) return st;
+    if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return FA2_ERR_ARG;
+    if (!workspace) return FA2_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA2_ERR_ALIGN;
+    if ((st = check_device()) != FA2_OK) return st;
+    const int S = num_splits == 0 ? auto_splits(B, H, Lq, Lk, causal) : num_splits;
+    if ((int64_t)p.n_wg * S > INT32_MAX) return FA2_ERR_DIM;
+    const int64_t rows = (int64_t)B * H * Lq;
+    if (!merge_grid_fits(rows, d)) return FA2_ERR_DIM;
+    const size_t need = workspace_bytes(S, B, H, Lq, d);
+    if (need == 0) return FA2_ERR_DIM;
+    if (workspace_bytes_given < need) return FA2_ERR_WORKSPACE;
+
+    float *o_parts = static_cast<float *>(workspace);
+    float *lse_parts = reinterpret_cast<float *>(static_cast<char *>(workspace) + partial_o_bytes(S, rows, d));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (S == 1) {                             // one range: the one-pass kernel
+        if (fa2::launch_fwd16(p, d, causal != 0, f16, fa2::FwdVariant::kPlain, s) != hipSuccess)
+            return FA2_ERR_LAUNCH;
+        return FA2_OK;
+    }
+    fa2::FwdParams pp = p;
+    pp.o = o_parts;
+    pp.lse = lse_parts;
+    pp.n_splits = S;
+    if (Lq <= fa2::kDecodeMaxRows) {          // a few query rows: the decoding kernel
+        pp.n_wg = B * H * S;
+        if (fa2::launch_decode(pp, d, f16, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    } else {
+        pp.n_wg = p.n_wg * S;
+        if (fa2::launch_fwd16(pp, d, causal != 0, f16, fa2::FwdVariant::kSplit, s) != hipSuccess)
+            return FA2_ERR_LAUNCH;
+    }
+    if (fa2::launch_merge(o_parts, lse_parts, S, rows, d, f16, o, lse, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+int merge16(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows, int d, void *o, float *lse,
+            bool f16, void *stream)
+{
+    if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL;
+    if (n_parts < 1 || n_parts > FA2_MAX_SPLITS) return FA2_ERR_ARG;
+    if (rows < 1) return FA2_ERR_DIM;
+    if (!head_dim_ok(d, kDims16)) return FA2_ERR_UNSUPPORTED_D;
+    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
+        return FA2_ERR_ALIGN;
+    if (!product_fits(n_parts, rows, d, sizeof(float))) return FA2_ERR_DIM;
+    if (!merge_grid_fits(rows, d)) return FA2_ERR_DIM;
+    int st = check_device();
+    if (st != FA2_OK) return st;
+    if (fa2::launch_merge(o_parts, lse_parts, n_parts, rows, d, f16, o, lse, static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+struct Window {
+    int left, right;
+};
+struct Dropout {
+    double p;
+    uint64_t seed;
+    uint32_t offset;
+};
+
+// The backward entry points: causal, or a window (w), with or without dropout (dr).
+int bwd16(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout, void *dq,
+          void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal, const Window *w,
+          const Dropout *dr, void *workspace, size_t workspace_bytes_given, bool f16, void *stream)
+{
+    fa2::BwdParams p;
+    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
+                         workspace_bytes_given, &p);
+    if (st != FA2_OK) return st;
+    if (dr && (st = dropout_setup(dr->p, dr->seed, dr->offset, &p.drop)) != FA2_OK) return st;
+    if ((st = check_device()) != FA2_OK) return st;
+    if (w) {
+        p.wl = w->left < 0 ? -1 : w->left;
+        p.wr = w->right < 0 ? -1 : w->right;
+    }
+    if (fa2::launch_bwd16(p, d, f16, dr != nullptr, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -253,25 +390,13 @@ int fa2_check_args(const void *q, const void *k, const void *v, const void *o, c
 int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
             int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
 {
-    fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
-    if (st != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    if (fa2::launch_fwd_bf16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    return fwd16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, false, stream);
 }
 
 int fa2_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse,
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream)
 {
-    fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
-    if (st != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    if (fa2::launch_fwd_f16(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    return fwd16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, true, stream);
 }
 
 int fa2_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
@@ -290,30 +415,28 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
                    int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
                    void *stream)
 {
-    fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, 0, 2, &p, kDims16);
-    if (st != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    // Negative bounds all mean "unbounded"; keep them as -1.
-    p.wl = window_left < 0 ? -1 : window_left;
-    p.wr = window_right < 0 ? -1 : window_right;
-    if (fa2::launch_fwd_bf16_window(p, d, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    return fwd_window16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_right, false, stream);
+}
+
+int fa2_fwd_window_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
+                       void *stream)
+{
+    return fwd_window16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, window_left, window_right, true, stream);
 }
 
 int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
                     double dropout_p, uint64_t seed, uint32_t offset, void *stream)
 {
-    fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
-    if (st != FA2_OK) return st;
-    if ((st = dropout_setup(dropout_p, seed, offset, &p.drop)) != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    if (fa2::launch_fwd_bf16_dropout(p, d, causal != 0, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    return fwd_dropout16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset, false, stream);
+}
+
+int fa2_fwd_dropout_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                        double dropout_p, uint64_t seed, uint32_t offset, void *stream)
+{
+    return fwd_dropout16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, dropout_p, seed, offset, true, stream);
 }
 
 int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal)
@@ -338,60 +461,28 @@ int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float 
                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
                     int num_splits, void *workspace, size_t workspace_bytes_given, void *stream)
 {
-    fa2::FwdParams p;
-    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
-    if (st != FA2_OK) return st;
-    if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return FA2_ERR_ARG;
-    if (!workspace) return FA2_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FA2_ERR_ALIGN;
-    if ((st = check_device()) != FA2_OK) return st;
-    const int S = num_splits == 0 ? auto_splits(B, H, Lq, Lk, causal) : num_splits;
-    if ((int64_t)p.n_wg * S > INT32_MAX) return FA2_ERR_DIM;
-    const int64_t rows = (int64_t)B * H * Lq;
-    if (!merge_grid_fits(rows, d)) return FA2_ERR_DIM;
-    const size_t need = workspace_bytes(S, B, H, Lq, d);
-    if (need == 0) return FA2_ERR_DIM;
-    if (workspace_bytes_given < need) return FA2_ERR_WORKSPACE;
+    return fwd_splitkv16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
+                         workspace_bytes_given, false, stream);
+}
 
-    float *o_parts = static_cast<float *>(workspace);
-    float *lse_parts = reinterpret_cast<float *>(static_cast<char *>(workspace) + partial_o_bytes(S, rows, d));
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (S == 1) {                             // one range: the one-pass kernel
-        if (fa2::launch_fwd_bf16(p, d, causal != 0, s) != hipSuccess) return FA2_ERR_LAUNCH;
-        return FA2_OK;
-    }
-    fa2::FwdParams pp = p;
-    pp.o = o_parts;
-    pp.lse = lse_parts;
-    pp.n_splits = S;
-    if (Lq <= fa2::kDecodeMaxRows) {          // a few query rows: the decoding kernel
-        pp.n_wg = B * H * S;
-        if (fa2::launch_decode(pp, d, s) != hipSuccess) return FA2_ERR_LAUNCH;
-    } else {
-        pp.n_wg = p.n_wg * S;
-        if (fa2::launch_fwd_bf16_split(pp, d, causal != 0, s) != hipSuccess) return FA2_ERR_LAUNCH;
-    }
-    if (fa2::launch_merge(o_parts, lse_parts, S, rows, d, o, lse, s) != hipSuccess) return FA2_ERR_LAUNCH;
-    return FA2_OK;
+int fa2_fwd_splitkv_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                        int num_splits, void *workspace, size_t workspace_bytes_given, void *stream)
+{
+    return fwd_splitkv16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
+                         workspace_bytes_given, true, stream);
 }
 
 int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                        int d, void *o, float *lse, void *stream)
 {
-    if (!o_parts || !lse_parts || !o || !lse) return FA2_ERR_NULL;
-    if (n_parts < 1 || n_parts > FA2_MAX_SPLITS) return FA2_ERR_ARG;
-    if (rows < 1) return FA2_ERR_DIM;
-    if (!head_dim_ok(d, kDims16)) return FA2_ERR_UNSUPPORTED_D;
-    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse))
-        return FA2_ERR_ALIGN;
-    if (!product_fits(n_parts, rows, d, sizeof(float))) return FA2_ERR_DIM;
-    if (!merge_grid_fits(rows, d)) return FA2_ERR_DIM;
-    int st = check_device();
-    if (st != FA2_OK) return st;
-    if (fa2::launch_merge(o_parts, lse_parts, n_parts, rows, d, o, lse, static_cast<hipStream_t>(stream)) !=
-        hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    return merge16(o_parts, lse_parts, n_parts, rows, d, o, lse, false, stream);
+}
+
+int fa2_merge_partials_f16(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
+                           int d, void *o, float *lse, void *stream)
+{
+    return merge16(o_parts, lse_parts, n_parts, rows, d, o, lse, true, stream);
 }
 
 size_t fa2_bwd_workspace_bytes(int B, int H, int Lq)
@@ -403,44 +494,16 @@ int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const fl
             void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
             void *workspace, size_t workspace_bytes_given, void *stream)
 {
-    fa2::BwdParams p;
-    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
-                         workspace_bytes_given, &p);
-    if (st != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    if (fa2::launch_bwd_bf16(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    return bwd16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, nullptr, nullptr,
+                 workspace, workspace_bytes_given, false, stream);
 }
 
 int fa2_bwd_f16(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                 void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
                 void *workspace, size_t workspace_bytes_given, void *stream)
 {
-    fa2::BwdParams p;
-    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
-                         workspace_bytes_given, &p);
-    if (st != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    if (fa2::launch_bwd_f16(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
-}
-
-int fa2_bwd_dropout(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
-                    void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
-                    double dropout_p, uint64_t seed, uint32_t offset, void *workspace,
-                    size_t workspace_bytes_given, void *stream)
-{
-    fa2::BwdParams p;
-    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, workspace,
-                         workspace_bytes_given, &p);
-    if (st != FA2_OK) return st;
-    if ((st = dropout_setup(dropout_p, seed, offset, &p.drop)) != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    if (fa2::launch_bwd_bf16_dropout(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    return bwd16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, nullptr, nullptr,
+                 workspace, workspace_bytes_given, true, stream);
 }
 
 int fa2_bwd_window(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
@@ -448,16 +511,39 @@ int fa2_bwd_window(const void *q, const void *k, const void *v, const void *o, c
                    int window_left, int window_right, void *workspace, size_t workspace_bytes_given,
                    void *stream)
 {
-    fa2::BwdParams p;
-    int st = prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, 0, workspace,
-                         workspace_bytes_given, &p);
-    if (st != FA2_OK) return st;
-    if ((st = check_device()) != FA2_OK) return st;
-    p.wl = window_left < 0 ? -1 : window_left;
-    p.wr = window_right < 0 ? -1 : window_right;
-    if (fa2::launch_bwd_bf16(p, d, o, lse, static_cast<hipStream_t>(stream)) != hipSuccess)
-        return FA2_ERR_LAUNCH;
-    return FA2_OK;
+    const Window w{window_left, window_right};
+    return bwd16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, 0, &w, nullptr, workspace,
+                 workspace_bytes_given, false, stream);
+}
+
+int fa2_bwd_window_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                       const void *dout, void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d,
+                       float scale, int window_left, int window_right, void *workspace,
+                       size_t workspace_bytes_given, void *stream)
+{
+    const Window w{window_left, window_right};
+    return bwd16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, 0, &w, nullptr, workspace,
+                 workspace_bytes_given, true, stream);
+}
+
+int fa2_bwd_dropout(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                    void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                    double dropout_p, uint64_t seed, uint32_t offset, void *workspace,
+                    size_t workspace_bytes_given, void *stream)
+{
+    const Dropout dr{dropout_p, seed, offset};
+    return bwd16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, nullptr, &dr, workspace,
+                 workspace_bytes_given, false, stream);
+}
+
+int fa2_bwd_dropout_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dout, void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d,
+                        float scale, int causal, double dropout_p, uint64_t seed, uint32_t offset,
+                        void *workspace, size_t workspace_bytes_given, void *stream)
+{
+    const Dropout dr{dropout_p, seed, offset};
+    return bwd16(q, k, v, o, lse, dout, dq, dk, dv, B, H, Lq, Lk, d, scale, causal, nullptr, &dr, workspace,
+                 workspace_bytes_given, true, stream);
 }
 
 const char *fa2_status_string(int status)

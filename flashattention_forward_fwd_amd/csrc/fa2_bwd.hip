@@ -708,31 +708,18 @@ hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const voi
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream)
-{
-    const int64_t rows = (int64_t)p.B * p.H * p.Lq;
-    const bool masked = p.wl >= 0 || p.wr >= 0;
-    hipError_t err = hipSuccess;
-    with_head_dim<true, true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, __bf16>(p, masked, rows, o, lse, stream); });
-    return err;
-}
-
-hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream)
-{
-    const int64_t rows = (int64_t)p.B * p.H * p.Lq;
-    const bool masked = p.wl >= 0 || p.wr >= 0;
-    hipError_t err = hipSuccess;
-    with_head_dim<true, true>(d, [&](auto dim) { err = launch_bwd_d<decltype(dim)::value, _Float16>(p, masked, rows, o, lse, stream); });
-    return err;
-}
-
-hipError_t launch_bwd_bf16_dropout(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream)
+hipError_t launch_bwd16(const BwdParams &p, int d, bool f16, bool dropout, const void *o, const float *lse,
+                        hipStream_t stream)
 {
     const int64_t rows = (int64_t)p.B * p.H * p.Lq;
     const bool masked = p.wl >= 0 || p.wr >= 0;
     hipError_t err = hipSuccess;
     with_head_dim<true, true>(d, [&](auto dim) {
-        err = launch_bwd_d<decltype(dim)::value, __bf16, true>(p, masked, rows, o, lse, stream);
+        constexpr int D = decltype(dim)::value;
+        if (f16) err = dropout ? launch_bwd_d<D, _Float16, true>(p, masked, rows, o, lse, stream)
+                               : launch_bwd_d<D, _Float16, false>(p, masked, rows, o, lse, stream);
+        else     err = dropout ? launch_bwd_d<D, __bf16, true>(p, masked, rows, o, lse, stream)
+                               : launch_bwd_d<D, __bf16, false>(p, masked, rows, o, lse, stream);
     });
     return err;
 }

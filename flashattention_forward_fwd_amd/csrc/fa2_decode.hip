@@ -29,8 +29,15 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 elements of E (bf16 or fp16) from their 16 raw bytes, widened to fp32.
+template <typename E>
+__device__ __forceinline__ f32x8 widen8(u32x4 raw)
+{
+    typedef E e8 __attribute__((ext_vector_type(8)));
+    return __builtin_convertvector(__builtin_bit_cast(e8, raw), f32x8);
+}
 
 constexpr int kDecodeThreads = 256;
 
@@ -61,7 +68,7 @@ __device__ __forceinline__ void combine(float (&m)[R], float (&l)[R], f32x8 (&ac
     }
 }
 
-template <int D, int R>
+template <int D, int R, typename E>
 __global__ __launch_bounds__(kDecodeThreads) void fa2_decode_kernel(FwdParams p)
 {
     using S = DecodeShape<D, R>;
@@ -88,7 +95,7 @@ __global__ __launch_bounds__(kDecodeThreads) void fa2_decode_kernel(FwdParams p)
         if (r < p.Lq && has_chunk)
             raw = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(p.q) +
                                                    ((size_t)bh * p.Lq + r) * D + 8 * chunk);
-        qv[r] = __builtin_convertvector(__builtin_bit_cast(bf16x8, raw), f32x8) * p.scale_log2;
+        qv[r] = widen8<E>(raw) * p.scale_log2;
     }
 
     float m[R], l[R];
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(kDecodeThreads) void fa2_decode_kernel(FwdParams p)
         float s[kUnroll][R];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const f32x8 kf = __builtin_convertvector(__builtin_bit_cast(bf16x8, kr[u]), f32x8);
+            const f32x8 kf = widen8<E>(kr[u]);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 float d = 0.0f;
@@ -150,7 +157,7 @@ __global__ __launch_bounds__(kDecodeThreads) void fa2_decode_kernel(FwdParams p)
             for (int u = 0; u < kUnroll; ++u) {
                 const float pu = __builtin_amdgcn_exp2f(s[u][r] - mn);
                 l[r] += pu;
-                acc[r] += pu * __builtin_convertvector(__builtin_bit_cast(bf16x8, vr[u]), f32x8);
+                acc[r] += pu * widen8<E>(vr[u]);
             }
             m[r] = mn;
         }
@@ -216,18 +223,27 @@ __global__ __launch_bounds__(kDecodeThreads) void fa2_decode_kernel(FwdParams p)
 
 }  // namespace
 
-hipError_t launch_decode(const FwdParams &p, int d, hipStream_t stream)
+namespace {
+template <typename E>
+void launch_decode_e(const FwdParams &p, int d, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kDecodeThreads);
     with_head_dim<true, true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
         switch (p.Lq) {
-        case 1: hipLaunchKernelGGL((fa2_decode_kernel<D, 1>), grid, block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((fa2_decode_kernel<D, 2>), grid, block, 0, stream, p); break;
-        case 3: hipLaunchKernelGGL((fa2_decode_kernel<D, 3>), grid, block, 0, stream, p); break;
-        default: hipLaunchKernelGGL((fa2_decode_kernel<D, 4>), grid, block, 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((fa2_decode_kernel<D, 1, E>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((fa2_decode_kernel<D, 2, E>), grid, block, 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((fa2_decode_kernel<D, 3, E>), grid, block, 0, stream, p); break;
+        default: hipLaunchKernelGGL((fa2_decode_kernel<D, 4, E>), grid, block, 0, stream, p); break;
         }
     });
+}
+}  // namespace
+
+hipError_t launch_decode(const FwdParams &p, int d, bool f16, hipStream_t stream)
+{
+    if (f16) launch_decode_e<_Float16>(p, d, stream);
+    else     launch_decode_e<__bf16>(p, d, stream);
     return hipGetLastError();
 }
 

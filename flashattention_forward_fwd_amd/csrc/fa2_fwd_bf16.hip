@@ -594,56 +594,40 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         p.lse[(size_t)bh * p.Lq + qrow] = (m + __builtin_amdgcn_logf(l)) * kLn2;
 }
 
-template <bool SPLIT, typename E = __bf16>
-hipError_t launch(const FwdParams &p, int d, bool causal, hipStream_t stream)
+template <typename E>
+hipError_t launch(const FwdParams &p, int d, bool causal, FwdVariant v, hipStream_t stream)
 {
     const dim3 grid(p.n_wg), block(kThreads);
     with_head_dim<true, true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
-        if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, SPLIT, false, E>), grid, block, 0, stream, p);
-        else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, SPLIT, false, E>), grid, block, 0, stream, p);
+        switch (v) {
+        case FwdVariant::kPlain:
+            if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, false, false, E>), grid, block, 0, stream, p);
+            else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, false, E>), grid, block, 0, stream, p);
+            break;
+        case FwdVariant::kSplit:
+            if (causal) hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, true, false, E>), grid, block, 0, stream, p);
+            else        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, true, false, E>), grid, block, 0, stream, p);
+            break;
+        case FwdVariant::kWindow:
+            hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, true, E>), grid, block, 0, stream, p);
+            break;
+        case FwdVariant::kDropout:
+            if (causal)
+                hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, false, false, E, true>), grid, block, 0, stream, p);
+            else
+                hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, false, E, true>), grid, block, 0, stream, p);
+            break;
+        }
     });
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t stream)
+hipError_t launch_fwd16(const FwdParams &p, int d, bool causal, bool f16, FwdVariant v, hipStream_t stream)
 {
-    return launch<false>(p, d, causal, stream);
-}
-
-hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream)
-{
-    return launch<true>(p, d, causal, stream);
-}
-
-hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t stream)
-{
-    return launch<false, _Float16>(p, d, causal, stream);
-}
-
-hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream)
-{
-    const dim3 grid(p.n_wg), block(kThreads);
-    with_head_dim<true, true>(d, [&](auto dim) {
-        constexpr int D = decltype(dim)::value;
-        hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, true>), grid, block, 0, stream, p);
-    });
-    return hipGetLastError();
-}
-
-hipError_t launch_fwd_bf16_dropout(const FwdParams &p, int d, bool causal, hipStream_t stream)
-{
-    const dim3 grid(p.n_wg), block(kThreads);
-    with_head_dim<true, true>(d, [&](auto dim) {
-        constexpr int D = decltype(dim)::value;
-        if (causal)
-            hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, true, false, false, __bf16, true>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((fa2_fwd_bf16_kernel<D, false, false, false, __bf16, true>), grid, block, 0, stream, p);
-    });
-    return hipGetLastError();
+    return f16 ? launch<_Float16>(p, d, causal, v, stream) : launch<__bf16>(p, d, causal, v, stream);
 }
 
 }  // namespace fa2

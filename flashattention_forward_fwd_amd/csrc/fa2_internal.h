@@ -114,7 +114,7 @@ __device__ __forceinline__ float halves_sum(float x)
 
 }  // namespace fa2
 
-// Host-side launchers (one per element type), defined next to their kernels.
+// Host-side launchers, defined next to their kernels.
 namespace fa2 {
 // Calls f(std::integral_constant<int, D>{}) for the head dimension d: 32, 64,
 // 128, 96 where WITH_96 (the 16-bit forward and backward kernels and the
@@ -129,26 +129,22 @@ inline void with_head_dim(int d, F f)
     else if (WITH_256 && d == 256) f(std::integral_constant<int, WITH_256 ? 256 : 128>{});
     else f(std::integral_constant<int, 128>{});
 }
-hipError_t launch_fwd_bf16(const FwdParams &p, int d, bool causal, hipStream_t stream);
+// The 16-bit forward kernels, bf16 or (f16) fp16 elements.  kSplit writes the
+// split-KV partials (p.o, p.lse: the fp32 partial arrays indexed by (split,
+// b*h, row)); kWindow takes its keys from p.wl, p.wr (causal unused); kDropout
+// applies p.drop.
+enum class FwdVariant { kPlain, kSplit, kWindow, kDropout };
+hipError_t launch_fwd16(const FwdParams &p, int d, bool causal, bool f16, FwdVariant v, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, bool causal, hipStream_t stream);
-hipError_t launch_fwd_f16(const FwdParams &p, int d, bool causal, hipStream_t stream);
-// Split-KV partials: p.o is the fp32 partial-output array, p.lse the partial
-// logsumexps, both indexed by (split, b*h, row).
-hipError_t launch_fwd_bf16_split(const FwdParams &p, int d, bool causal, hipStream_t stream);
-// Window forward: p.wl, p.wr select the visible keys (bf16, one pass).
-hipError_t launch_fwd_bf16_window(const FwdParams &p, int d, hipStream_t stream);
-// Dropout forward: p.drop selects the keep mask (bf16, one pass).
-hipError_t launch_fwd_bf16_dropout(const FwdParams &p, int d, bool causal, hipStream_t stream);
 // Backward: D and lse2 into p.delta / p.lse2 from o and lse, then dK/dV, then dQ,
-// for the keys p.wl / p.wr leave visible.
-hipError_t launch_bwd_bf16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
-hipError_t launch_bwd_f16(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
-// Backward of the dropout forward (bf16): p.drop as given to that forward.
-hipError_t launch_bwd_bf16_dropout(const BwdParams &p, int d, const void *o, const float *lse, hipStream_t stream);
+// for the keys p.wl / p.wr leave visible; dropout: the keep mask of p.drop.
+hipError_t launch_bwd16(const BwdParams &p, int d, bool f16, bool dropout, const void *o, const float *lse,
+                        hipStream_t stream);
+// Merge of split partials into o (bf16, or fp16 where f16) and lse.
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
-                        int d, void *o, float *lse, hipStream_t stream);
-// Split-KV partials for Lq <= kDecodeMaxRows (bf16), same outputs as
-// launch_fwd_bf16_split; p.n_wg = B * H * p.n_splits.
+                        int d, bool f16, void *o, float *lse, hipStream_t stream);
+// Split-KV partials for Lq <= kDecodeMaxRows, same outputs as the kSplit
+// forward; p.n_wg = B * H * p.n_splits.
 constexpr int kDecodeMaxRows = 4;
-hipError_t launch_decode(const FwdParams &p, int d, hipStream_t stream);
+hipError_t launch_decode(const FwdParams &p, int d, bool f16, hipStream_t stream);
 }  // namespace fa2

@@ -10,7 +10,8 @@
 // section 4.3): rescale every part by the global max, sum, normalise.
 //
 // The kernel is bound by HBM bandwidth (it reads n_parts (d + 1) fp32 values
-// and writes d bf16 values plus one fp32 per row), so it is laid out for
+// and writes d 16-bit values (bf16 or fp16, round to nearest even) plus one fp32
+// per row), so it is laid out for
 // coalescing, not for the matrix cores: d/4 consecutive threads own one row,
 // each reading 16 contiguous bytes of every part and writing 8 bytes of O.
 #include "fa2_internal.h"
@@ -19,16 +20,16 @@ namespace fa2 {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMergeThreads = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <int D>
+template <int D, typename E>
 __global__ __launch_bounds__(kMergeThreads)
 void fa2_merge_kernel(const float *__restrict__ o_parts, const float *__restrict__ lse_parts,
                       int n_parts, int64_t rows, uint16_t *__restrict__ o, float *__restrict__ lse)
 {
+    typedef E e4 __attribute__((ext_vector_type(4)));
     constexpr int kThreadsPerRow = D / 4;
     const int64_t g = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
     const int64_t row = g / kThreadsPerRow;
@@ -53,8 +54,7 @@ void fa2_merge_kernel(const float *__restrict__ o_parts, const float *__restrict
         }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    const bf16x4 b4 = __builtin_convertvector(acc * inv, bf16x4);
-    *reinterpret_cast<bf16x4 *>(o + row * D + 4 * c) = b4;
+    *reinterpret_cast<e4 *>(o + row * D + 4 * c) = __builtin_convertvector(acc * inv, e4);
     if (c == 0)
         lse[row] = wsum > 0.f ? mx + __builtin_amdgcn_logf(wsum) * kLn2 : -INFINITY;
 }
@@ -62,14 +62,19 @@ void fa2_merge_kernel(const float *__restrict__ o_parts, const float *__restrict
 }  // namespace
 
 hipError_t launch_merge(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
-                        int d, void *o, float *lse, hipStream_t stream)
+                        int d, bool f16, void *o, float *lse, hipStream_t stream)
 {
     const int64_t threads = rows * (d / 4);
     const dim3 grid((unsigned)((threads + kMergeThreads - 1) / kMergeThreads)), block(kMergeThreads);
     uint16_t *ob = static_cast<uint16_t *>(o);
     with_head_dim<true, true>(d, [&](auto dim) {
         constexpr int D = decltype(dim)::value;
-        hipLaunchKernelGGL((fa2_merge_kernel<D>), grid, block, 0, stream, o_parts, lse_parts, n_parts, rows, ob, lse);
+        if (f16)
+            hipLaunchKernelGGL((fa2_merge_kernel<D, _Float16>), grid, block, 0, stream, o_parts, lse_parts, n_parts,
+                               rows, ob, lse);
+        else
+            hipLaunchKernelGGL((fa2_merge_kernel<D, __bf16>), grid, block, 0, stream, o_parts, lse_parts, n_parts,
+                               rows, ob, lse);
     });
     return hipGetLastError();
 }

@@ -125,6 +125,11 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
                    int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
                    void *stream);
 
+/* fa2_fwd_window on fp16 q, k, v, o (precision as fa2_fwd_f16). */
+int fa2_fwd_window_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
+                       void *stream);
+
 /*
  * Forward pass with dropout on the attention probabilities, bf16.  "Flash
  * Attention 全解析（上）", section 2.1.2, lists dropout among the steps fused into
@@ -146,6 +151,11 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
 int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
                     double dropout_p, uint64_t seed, uint32_t offset, void *stream);
+
+/* fa2_fwd_dropout on fp16 q, k, v, o (the same keep mask; precision as fa2_fwd_f16). */
+int fa2_fwd_dropout_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                        double dropout_p, uint64_t seed, uint32_t offset, void *stream);
 
 /*
  * Split-KV forward (FlashDecoding): the same result as fa2_fwd, computed in two
@@ -185,6 +195,12 @@ int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float 
 int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
                     int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/* fa2_fwd_splitkv on fp16 q, k, v, o (the same workspace; o rounded to fp16, nearest
+ * even, by the merge). */
+int fa2_fwd_splitkv_f16(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int B, int H, int Lq, int Lk, int d, float scale, int causal,
+                        int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Workspace bytes fa2_fwd_splitkv needs for these sizes: num_splits * B * H * Lq
@@ -227,6 +243,10 @@ int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal);
  */
 int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                        int d, void *o, float *lse, void *stream);
+
+/* fa2_merge_partials writing fp16 o (round to nearest even). */
+int fa2_merge_partials_f16(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
+                           int d, void *o, float *lse, void *stream);
 
 /*
  * Backward pass (gradients) of fa2_fwd, bf16.  Given the forward's inputs, its
@@ -286,6 +306,12 @@ int fa2_bwd_dropout(const void *q, const void *k, const void *v, const void *o, 
                     double dropout_p, uint64_t seed, uint32_t offset, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* fa2_bwd_dropout on fp16 data (the backward of fa2_fwd_dropout_f16). */
+int fa2_bwd_dropout_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                        const void *dout, void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d,
+                        float scale, int causal, double dropout_p, uint64_t seed, uint32_t offset,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /*
  * Backward pass of fa2_fwd_window: the gradients of attention over the key
  * window (window_left, window_right) of fa2_fwd_window, from its o and lse.
@@ -295,6 +321,12 @@ int fa2_bwd_dropout(const void *q, const void *k, const void *v, const void *o, 
 int fa2_bwd_window(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                    void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale,
                    int window_left, int window_right, void *workspace, size_t workspace_bytes, void *stream);
+
+/* fa2_bwd_window on fp16 data (the backward of fa2_fwd_window_f16). */
+int fa2_bwd_window_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                       const void *dout, void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d,
+                       float scale, int window_left, int window_right, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /*
  * Workspace bytes fa2_bwd needs: lse * log2(e) for the B*H*Lq query rows and,

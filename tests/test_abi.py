@@ -25,7 +25,21 @@ def test_header_declares_the_entry_points():
                                          "fa2_splitkv_num_splits", "fa2_merge_partials",
                                          "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_fwd_window",
                                          "fa2_bwd_window", "fa2_bwd_f16", "fa2_fwd_dropout",
-                                         "fa2_bwd_dropout"])
+                                         "fa2_bwd_dropout", "fa2_fwd_window_f16", "fa2_fwd_dropout_f16",
+                                         "fa2_fwd_splitkv_f16", "fa2_merge_partials_f16",
+                                         "fa2_bwd_window_f16", "fa2_bwd_dropout_f16"])
+
+
+def test_f16_twins_reject_like_their_bf16_entry_points():
+    L = fa.lib()
+    big = 1 << 30
+    assert L.fa2_fwd_window_f16(None, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 4, 0, None) == 1
+    assert L.fa2_fwd_window_f16(A, A, A, A, A, 1, 1, 8, 8, 80, 0.1, 4, 0, None) == 3
+    assert L.fa2_fwd_dropout_f16(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 1, 1.0, 1, 0, None) == 4
+    assert L.fa2_fwd_splitkv_f16(A, A, A, A, A, 1, 1, 8, 8, 64, 0.1, 0, -1, A, big, None) == 4
+    assert L.fa2_merge_partials_f16(A, A, 0, 10, 64, A, A, None) == 4
+    assert L.fa2_bwd_window_f16(*([A] * 9), 1, 1, 8, 8, 64, 0.1, 4, 0, A, 4, None) == 8
+    assert L.fa2_bwd_dropout_f16(*([A] * 9), 1, 1, 8, 8, 64, 0.1, 1, -0.5, 1, 0, A, big, None) == 4
 
 
 def test_library_exports_every_declared_symbol():
