@@ -36,13 +36,17 @@ void fa2_merge_kernel(const float *__restrict__ o_parts, const float *__restrict
     const int c = (int)(g % kThreadsPerRow);        // this thread's 4 columns: 4c .. 4c + 3
     if (row >= rows) return;
 
+    // Unrolled so the loads of several parts are in flight together (the part
+    // loops are latency-bound when rows are few and parts many, as in decoding).
     float mx = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < n_parts; ++s)
         mx = fmaxf(mx, lse_parts[(size_t)s * rows + row]);
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (mx != -INFINITY) {
+#pragma unroll 4
         for (int s = 0; s < n_parts; ++s) {
             const float ls = lse_parts[(size_t)s * rows + row];
             if (ls == -INFINITY) continue;          // empty part: its O_s was never written
