@@ -40,15 +40,20 @@ CONTEXT = {
 
 
 def kernel_source_digest():
-    """sha256 over the sources of the one-pass forward kernel and its launch (the
-    kernel file, the shared headers and the entry points), to tell whether stored
-    counters are stale.  The backward, merge and fp32 sources do not enter it."""
+    """sha256 over the code of the one-pass forward kernel and its launch (the
+    kernel file, the shared headers and the entry points; comments and blank
+    space removed), to tell whether stored counters are stale.  The backward,
+    merge and fp32 sources do not enter it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "flashattention_forward_fwd_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith(".h") or name in ("fa2_fwd_bf16.hip", "fa2_api.hip"):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name)) as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)      # block comments
+            text = re.sub(r"//[^\n]*", " ", text)                    # line comments
+            text = " ".join(text.split())
+            h.update(name.encode() + b"\0" + text.encode())
     return h.hexdigest()[:16]
 
 

@@ -1,4 +1,6 @@
-// fa2_fwd_bf16.hip -- FlashAttention-2 forward, bf16 in/out, for gfx950.
+// fa2_fwd_bf16.hip -- FlashAttention-2 forward with 16-bit (bf16 or fp16) in/out,
+// for gfx950: one kernel template serves the one-pass forward, the split-KV
+// partials, the sliding window and dropout, at head dimensions 32 to 256.
 //
 // One work-group owns kBr = 128 query rows of one (batch, head) and streams the
 // K/V tiles of that head through LDS (the Q-outer / KV-inner order and the
