@@ -339,9 +339,9 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int Lq);
 const char *fa2_status_string(int status);
 
 /*
- * Validate arguments exactly as fa2_fwd / fa2_fwd_f32 do, without any HIP call.
- * elem_bytes is 2 (bf16) or 4 (fp32).  Returns the status those entry points
- * would return before launching.
+ * Validate arguments exactly as fa2_fwd / fa2_fwd_f16 / fa2_fwd_f32 do, without any
+ * HIP call.  elem_bytes is 2 (bf16 or fp16) or 4 (fp32).  Returns the status those
+ * entry points would return before launching.
  */
 int fa2_check_args(const void *q, const void *k, const void *v, const void *o, const float *lse,
                    int B, int H, int Lq, int Lk, int d, float scale, int causal, int elem_bytes);
