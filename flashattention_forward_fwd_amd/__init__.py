@@ -23,6 +23,19 @@ __all__ = ["forward", "backward", "merge_partials", "FA2Error", "status_string",
     sorted(n for n in _lib.SIGNATURES if n.startswith("fa2_") and n not in ("fa2_status_string",))
 
 
+def _check_buffer(t, shape, dtype, device, name):
+    """A caller-provided output or workspace must be exactly what the kernels will
+    write: the library trusts shapes and never sees strides."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be a device tensor on %s" % (name, device))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, not %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
 def _entry(name, dtype):
     """The bf16 entry point `name` or its fp16 twin for torch dtype `dtype`."""
     import torch
@@ -65,13 +78,19 @@ def forward(q, k, v, causal=False, scale=None, out=None, lse=None, num_splits=No
     Lk = k.shape[2]
     if tuple(k.shape) != (B, H, Lk, d) or tuple(v.shape) != (B, H, Lk, d):
         raise ValueError("k and v must be [B, H, Lk, d] matching q")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on one device")
     q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    _check_buffer(lse, (B, H, Lq), torch.float32, q.device, "lse")
+    if workspace is not None:
+        _check_buffer(workspace, None, None, q.device, "workspace")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     c = int(bool(causal))
     if (dropout is not None or window is not None or num_splits is not None) and q.dtype == torch.float32:
@@ -126,10 +145,14 @@ def merge_partials(o_parts, lse_parts, out=None, lse=None, dtype=None):
         dtype = out.dtype if out is not None else torch.bfloat16
     if dtype not in (torch.bfloat16, torch.float16) or (out is not None and out.dtype != dtype):
         raise ValueError("the merged output is bfloat16 or float16")
+    if lse_parts.device != o_parts.device:
+        raise ValueError("o_parts and lse_parts must be on one device")
     if out is None:
         out = torch.empty(o_parts.shape[1:], dtype=dtype, device=o_parts.device)
+    _check_buffer(out, o_parts.shape[1:], dtype, o_parts.device, "out")
     if lse is None:
         lse = torch.empty(lse_parts.shape[1:], dtype=torch.float32, device=o_parts.device)
+    _check_buffer(lse, lse_parts.shape[1:], torch.float32, o_parts.device, "lse")
     stream = torch.cuda.current_stream(o_parts.device).cuda_stream
     _entry("fa2_merge_partials", dtype)(o_parts, lse_parts, S, rows, d, out, lse, stream)
     return out, lse
@@ -165,17 +188,22 @@ def backward(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, 
         raise ValueError("k and v must be [B, H, Lk, d] matching q")
     if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, H, Lq):
         raise ValueError("o and dout must have q's shape and lse [B, H, Lq]")
+    if any(t.device != q.device for t in ts + (lse,)):
+        raise ValueError("all tensors must be on one device")
     q, k, v, o, dout, lse = (t.contiguous() for t in (q, k, v, o, dout, lse))
     if scale is None:
         scale = float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32))
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for t, like, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _check_buffer(t, like.shape, like.dtype, q.device, name)
     need = fa2_bwd_workspace_bytes(B, H, Lq)
     if need == 0:
         raise ValueError("sizes rejected by fa2_bwd_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_buffer(workspace, None, None, q.device, "workspace")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     nbytes = workspace.numel() * workspace.element_size()
     if dropout is not None:

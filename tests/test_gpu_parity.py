@@ -186,3 +186,24 @@ def test_output_rows_all_written():
     fa.forward(q, k, v, causal=True, out=o, lse=lse)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_wrapper_rejects_mismatched_outputs():
+    """The library trusts shapes; the Python wrapper refuses outputs it would overrun."""
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(1, 2, 64, device="cuda")
+    bad_outs = [torch.zeros(1, 2, 32, 64, dtype=torch.bfloat16, device="cuda"),        # too small
+                torch.zeros(1, 2, 64, 64, dtype=torch.float16, device="cuda"),         # wrong dtype
+                torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device="cuda")[..., ::2]]   # strided
+    for out in bad_outs:
+        with pytest.raises(ValueError):
+            fa.forward(q, q, q, out=out, lse=lse)
+    with pytest.raises(ValueError):
+        fa.forward(q, q, q, lse=torch.zeros(1, 2, 32, device="cuda"))
+    o, l = fa.forward(q, q, q)
+    with pytest.raises(ValueError):
+        fa.backward(q, q, q, o, l, q, dq=torch.zeros(1, 2, 64, 32, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.merge_partials(torch.zeros(2, 3, 64, device="cuda"), torch.zeros(2, 3, device="cuda"),
+                          out=torch.zeros(2, 64, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
