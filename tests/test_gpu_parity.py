@@ -207,3 +207,46 @@ def test_wrapper_rejects_mismatched_outputs():
         fa.merge_partials(torch.zeros(2, 3, 64, device="cuda"), torch.zeros(2, 3, device="cuda"),
                           out=torch.zeros(2, 64, dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("path", ["one-pass", "split-decode", "split-mfma"])
+def test_max_keys_per_head(path):
+    """Lk at the one-head limit ((Lk + 64) d 2 bytes < 2^31 at d = 128: 32-bit tile
+    offsets up to 2 GiB).  K = 0 except five hot keys (first, early, middle, in the
+    last full tile, last) whose first component is 1; V = 1 except distinct hot rows.
+    With scale 1, a query 30 e_0 scores 30 on the hot keys and 0 elsewhere, so
+    O = ((Lk - h) + e^30 sum V_hot) / Z and LSE = ln Z, Z = (Lk - h) + h e^30, in closed
+    form; query 0 gives the plain mean over all Lk keys; query -30 e_0 almost only
+    the ones."""
+    d, Lk = 128, (1 << 23) - 65
+    Lq = 5 if path == "split-mfma" else 3
+    say("case max keys per head: Lk=%d d=%d path=%s" % (Lk, d, path))
+    hot = np.array([0, 1000, Lk // 2 + 17, Lk - 70, Lk - 1])
+    h = len(hot)
+    q = torch.zeros(1, 1, Lq, d, dtype=torch.bfloat16, device="cuda")
+    q[0, 0, 0, 0] = 30.0
+    q[0, 0, 2, 0] = -30.0
+    if Lq > 3:
+        q[0, 0, 3:, 0] = 30.0
+    k = torch.zeros(1, 1, Lk, d, dtype=torch.bfloat16, device="cuda")
+    k[0, 0, torch.from_numpy(hot).cuda(), 0] = 1.0
+    v = torch.ones(1, 1, Lk, d, dtype=torch.bfloat16, device="cuda")
+    vh = (torch.arange(h, dtype=torch.float32)[:, None] * 0.5 + 2.0 +
+          torch.arange(d, dtype=torch.float32)[None, :] / 64.0).to(torch.bfloat16)
+    v[0, 0, torch.from_numpy(hot).cuda()] = vh.cuda()
+    splits = None if path == "one-pass" else 0
+    o, lse = fa.forward(q, k, v, scale=1.0, num_splits=splits)
+    torch.cuda.synchronize()
+    o, lse = o[0, 0].double().cpu().numpy(), lse[0, 0].double().cpu().numpy()
+    del k, v
+    vsum = vh.double().numpy().sum(axis=0)
+    n = Lk - h
+    want_o, want_l = [], []
+    for s in [30.0, 0.0, -30.0] + [30.0] * (Lq - 3):
+        z = n + h * np.exp(s)
+        want_o.append((n + np.exp(s) * vsum) / z)
+        want_l.append(np.log(z))
+    eo = float(np.max(np.abs(o - np.array(want_o))))
+    el = float(np.max(np.abs(lse - np.array(want_l))))
+    say("  max|dO|=%.3e  max|dLSE|=%.3e" % (eo, el))
+    assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
