@@ -32,6 +32,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X fp32, published
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_bf16_B2_H32_L4096_d128_causal_traffic.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa2_fwd_bf16_B2_H32_L4096_d128_causal_counters.md")
 CONTEXT = {
     "a100_fp16_tensor_tflops": 312, "a100_hbm_gbs": 1555, "a100_sram_tbs": 19,
     "claimed_matmul_utilisation_fa1_to_fa2": "30-50% -> >70%",
@@ -57,11 +58,11 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload_name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    when the summary is missing, covers another workload, or predates the kernel."""
+def stored_fields(path, workload_name):
+    """The machine-readable fields of a committed rocprofv3 summary, or None when
+    the summary is missing, covers another workload, or predates the kernel."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
@@ -69,10 +70,32 @@ def stored_traffic(workload_name):
         return None
     if fields.get("kernel_source_sha256") != kernel_source_digest():
         return None
+    return fields
+
+
+def stored_traffic(workload_name):
+    """HBM bytes per launch from the committed counter summary (or None)."""
+    fields = stored_fields(TRAFFIC_FILE, workload_name)
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields["hbm_bytes_per_launch"]) if fields else None
     except (KeyError, ValueError):
         return None
+
+
+def stored_counters(workload_name):
+    """MFMA-busy fraction, VALU and LDS instruction mix and LDS bank conflicts of
+    the forward kernel, from the committed counter summary (or None)."""
+    fields = stored_fields(COUNTERS_FILE, workload_name)
+    if not fields:
+        return None
+    keys = ("mfma_busy_frac", "clock_ghz", "valu_coexec_frac", "valu_insts_per_score_element",
+            "trans_insts_per_score_element", "lds_insts_per_wave_tile", "lds_bank_conflict_cycles")
+    try:
+        out = {k: float(fields[k]) for k in keys}
+    except (KeyError, ValueError):
+        return None
+    out["source"] = os.path.join("profiles", os.path.basename(COUNTERS_FILE))
+    return out
 
 
 def cpu_baseline(w, q, k, v, rows_per_head):
@@ -315,6 +338,10 @@ def main():
         "roofline": roof,
         "context_pages": CONTEXT,
     }
+    plain = split_info is None and bwd_info is None and win_info is None and drop_info is None and not args.fp16
+    counters = stored_counters(w.name) if plain else None
+    if counters is not None:
+        out["counters"] = counters
     if split_info is not None:
         out["config"]["split_kv"] = split_info
     if args.fp16:
