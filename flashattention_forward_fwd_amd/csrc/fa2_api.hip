@@ -553,7 +553,9 @@ const char *fa2_status_string(int status)
     case FA2_ERR_NULL: return "a tensor pointer is NULL";
     case FA2_ERR_DIM: return "B, H, Lq, Lk must be positive and the sizes must fit (one head's K below 2 GiB)";
     case FA2_ERR_UNSUPPORTED_D: return "head dimension d must be 32, 64 or 128 (or 96 or 256 for 16-bit data)";
-    case FA2_ERR_ARG: return "causal must be 0 or 1 and scale finite and positive";
+    case FA2_ERR_ARG:
+        return "an argument is out of range: causal must be 0 or 1, scale finite and positive, "
+               "num_splits in [0, FA2_MAX_SPLITS], dropout_p in [0, 1)";
     case FA2_ERR_ALIGN: return "tensor pointers must be 16-byte aligned";
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";
     case FA2_ERR_LAUNCH: return "kernel launch failed";

@@ -69,7 +69,8 @@ typedef enum fa2_status {
                                     head's K exceeds 2^31 - 1 bytes */
     FA2_ERR_UNSUPPORTED_D = 3,   /* head dimension d not in {32, 64, 128}, or 96 / 256 for
                                     the bf16/fp16 entry points and the merge */
-    FA2_ERR_ARG = 4,             /* causal not 0 or 1, or scale not finite or <= 0 */
+    FA2_ERR_ARG = 4,             /* causal not 0 or 1, scale not finite or <= 0, num_splits or
+                                    dropout_p out of range */
     FA2_ERR_ALIGN = 5,           /* a tensor pointer is not 16-byte aligned */
     FA2_ERR_DEVICE = 6,          /* no usable HIP device, or the device is not gfx950 */
     FA2_ERR_LAUNCH = 7,          /* the kernel launch was refused by the runtime */
