@@ -1,4 +1,4 @@
-"""The entry points under HIP graph capture and on a non-default stream.
+"""The entry points under HIP graph capture, on side streams and without allocation.
 
 Every entry point enqueues its kernels on the caller's stream and allocates
 nothing, so a caller can capture a call (with preallocated outputs and workspace)
@@ -97,3 +97,49 @@ def test_non_default_stream():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
     assert np.isfinite(o2.float().cpu().numpy()).all()
+
+
+def test_preallocated_calls_allocate_nothing():
+    """With outputs and workspace passed in, forward (one-pass and split-KV) and
+    backward allocate no device memory (the library allocates none itself)."""
+    say("case no allocation with caller buffers: forward, split-KV, backward (1, 2, 640, 640, 64)")
+    q, k, v = (t.cuda() for t in random_qkv(1, 2, 640, 640, 64, "bf16", seed=76))
+    do = random_dout(1, 2, 640, 64, "bf16", seed=76).cuda()
+    o, lse = torch.empty_like(q), torch.empty(1, 2, 640, device="cuda")
+    ws = torch.empty(fa.fa2_splitkv_workspace_bytes(1, 2, 640, 640, 64, 1, 3), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(fa.fa2_bwd_workspace_bytes(1, 2, 640), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa.forward(q, k, v, causal=True, out=o, lse=lse)          # warm-up (library load)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    fa.forward(q, k, v, causal=True, out=o, lse=lse)
+    fa.forward(q, k, v, causal=True, num_splits=3, workspace=ws, out=o, lse=lse)
+    fa.backward(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, workspace=bws)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+
+
+def test_two_streams_concurrently():
+    """Calls in flight on two streams at once (different inputs, shared library
+    state) give the results each gives alone."""
+    say("case two streams: forward + backward on (1, 4, 900, 900, 128) and (2, 2, 333, 777, 64)")
+    shapes = [((1, 4, 900, 900, 128), True, 77), ((2, 2, 333, 777, 64), False, 78)]
+    ins, alone = [], []
+    for (B, H, Lq, Lk, d), causal, seed in shapes:
+        q, k, v = (t.cuda() for t in random_qkv(B, H, Lq, Lk, d, "bf16", seed=seed))
+        do = random_dout(B, H, Lq, d, "bf16", seed=seed).cuda()
+        o, lse = fa.forward(q, k, v, causal=causal)
+        alone.append((o, lse) + tuple(fa.backward(q, k, v, o, lse, do, causal=causal)))
+        ins.append((q, k, v, do, causal))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    got = [None, None]
+    for _ in range(3):
+        for i, (s, (q, k, v, do, causal)) in enumerate(zip(streams, ins)):
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                o, lse = fa.forward(q, k, v, causal=causal)
+                got[i] = (o, lse) + tuple(fa.backward(q, k, v, o, lse, do, causal=causal))
+        torch.cuda.synchronize()
+        for a, b in zip(got, alone):
+            assert all(torch.equal(x, y) for x, y in zip(a, b))
