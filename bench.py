@@ -183,9 +183,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the forward pass shards by (batch, head) and query tile with no exchange; "
-              "no multi-GPU run is part of it)" % args.gpus, file=sys.stderr)
+        print("bench.py: the library and this bench run on one GPU; --gpus %d is not supported "
+              "(the forward pass would shard by (batch, head) and query tile with no exchange; "
+              "there is no multi-GPU path)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
