@@ -170,6 +170,17 @@ __device__ __forceinline__ void load_tile_async(__amdgpu_buffer_rsrc_t src, int 
     }
 }
 
+// Where a step issues the copies of the next tiles: at its start, or (d = 64)
+// after its P~V products, from a closure the loop passes in.  Measured on MI355X,
+// the d = 64 loop written that way compiles to 156 VGPRs instead of 210, so three
+// work-groups share a CU (LDS allows it at d = 64), and runs 8-11 % faster; the
+// same form costs up to 3 % at d = 32 and 3-20 % at d >= 96 (issued late), so
+// every other head dimension keeps the copies at the start of the step.
+template <int D> constexpr bool kLateTileLoads = D == 64;
+struct NoTileLoads {
+    __device__ void operator()() const {}
+};
+
 // Threshold (base-2 units) for moving the running max.  While a row's max has
 // not grown by more than this, the old reference max is kept: P~ = 2^(S c - m)
 // is then at most 2^8, l and O~ keep the same reference, and nothing is
@@ -315,9 +326,12 @@ __device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, f
 
 // One step of the pipelined loop for tile j: probabilities of tile j (VALU)
 // while the scores of tile j+1 run (MFMA), then O~ += P~_j V_j (MFMA) while the
-// max of tile j+1 is taken (VALU).
-template <int D, typename E, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW, bool DROPOUT>
-__device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const LDS_AS char *v_cur,
+// max of tile j+1 is taken (VALU).  Where kLateTileLoads<D>, the step issues the
+// copies of the next tiles (late_loads) after its P~V products; otherwise the
+// caller has issued them before the step.
+template <int D, typename E, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW, bool DROPOUT,
+          typename Loads = NoTileLoads>
+__device__ __forceinline__ void pipelined_step(Loads &&late_loads, const LDS_AS char *k_next, const LDS_AS char *v_cur,
                                                const typename V16<E>::x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
                                                f32x16 (&s_cur)[2], float &m, float &lpart, float &alpha,
                                                float c2, int j, int t0, int plain_lo, int n_plain, int Lk,
@@ -331,6 +345,7 @@ __device__ __forceinline__ void pipelined_step(const LDS_AS char *k_next, const 
     f32x16 s_next[2];
     scores<D, E>(k_next, qf, s_next, k_lane);
     accumulate_pv<D, E>(v_cur, pf, acc_o, v_lane);
+    if constexpr (kLateTileLoads<D>) late_loads();
     float mt = row_max_scaled(s_next, c2);
     // The row sum and the next max are consumed after the branch below; this
     // use keeps their VALU work in this block, between the MFMAs, instead of
@@ -517,11 +532,36 @@ void fa2_fwd_bf16_kernel(FwdParams p)
     // Every wavefront passes the same n_kv barriers.  The pipelined loop is
     // unrolled over two tiles so each buffer is fixed at compile time.
     int j = 0;
+    if constexpr (kLateTileLoads<D>) {
+        while (j + 1 < n_wave) {
+            // as below, with the copies of the next tiles issued inside the step
+            auto loads_even = [&]() {
+                if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK0, wave, loff);
+                load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
+            };
+            pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(loads_even,
+                (const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+                plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (++j + 1 >= n_wave) break;
+            auto loads_odd = [&]() {
+                if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK1, wave, loff);
+                load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
+            };
+            pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(loads_odd,
+                (const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+                plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            ++j;
+        }
+    } else {
     while (j + 1 < n_wave) {
         // even tile j: K_{j+1} in sK1, V_j in sV0; loads K_{j+2} -> sK0, V_{j+1} -> sV1
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK0, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
-        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(
+        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(NoTileLoads{},
             (const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
             plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
@@ -530,12 +570,13 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         // odd tile j: K_{j+1} in sK0, V_j in sV1; loads K_{j+2} -> sK1, V_{j+1} -> sV0
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK1, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
-        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(
+        pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(NoTileLoads{},
             (const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
             plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         ++j;
+    }
     }
     if (j < n_wave) {                         // last computed tile: no next scores
         const bool odd = j & 1;
