@@ -215,17 +215,30 @@ __device__ __forceinline__ void scores(const LDS_AS char *kb, const typename V16
 }
 
 // Keys past Lk, (causal) keys after the lane's query and (window) keys outside
-// [qrow - wl, qrow + wr] get -inf.
+// [qrow - wl, qrow + wr] get -inf.  Element (t, i) of this lane holds key
+// k0 + 4 hh + off(t, i), off = 32 t + 8 (i / 4) + i % 4; without a window the
+// visible keys are those up to one last key, so each element costs one compare
+// of the constant off against a per-lane limit and one select.
 template <bool CAUSAL, bool WINDOW>
 __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int k0, int Lk, int qrow, int hh, int wl, int wr)
 {
+    if (!WINDOW) {
+        const int last = CAUSAL ? min(qrow, Lk - 1) : Lk - 1;      // last visible key
+        const int lim = last - k0 - 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                s[t][i] = 32 * t + 8 * (i / 4) + (i % 4) > lim ? -INFINITY : s[t][i];
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
             bool hidden = key >= Lk || (CAUSAL && key > qrow);
-            if (WINDOW) hidden = hidden || (wl >= 0 && key < qrow - wl) || (wr >= 0 && key > qrow + wr);
+            hidden = hidden || (wl >= 0 && key < qrow - wl) || (wr >= 0 && key > qrow + wr);
             s[t][i] = hidden ? -INFINITY : s[t][i];
         }
 }
@@ -244,21 +257,24 @@ __device__ __forceinline__ float row_max_scaled(const f32x16 (&s)[2], float c2)
 }
 
 // Moves the reference max when some row of the wavefront grew past the
-// threshold; returns the factor O~ and l must be multiplied by (1: no move).
+// threshold, and rescales O~ and l by alpha = 2^(m - m') right there: the branch
+// is the same on every lane and rarely taken, so the common step spends no
+// exponential or select on it.
 // EMPTY_ROWS: a row may have seen no visible key yet (m = -inf; only in a
 // causal K/V range that starts after some of the wavefront's rows).  Such a
 // row keeps m = -inf and alpha = 1 until its first visible key arrives.
-template <bool EMPTY_ROWS>
-__device__ __forceinline__ float update_max(float &m, float m_tile)
+template <int D, bool EMPTY_ROWS>
+__device__ __forceinline__ void update_max(float &m, float m_tile, f32x16 (&acc_o)[D / 32], float &lpart)
 {
     const float m_cand = fmaxf(m, m_tile);
-    float alpha = 1.0f;
-    if (__builtin_amdgcn_ballot_w64(m_cand - m > kRescaleThreshold) != 0) {
-        alpha = __builtin_amdgcn_exp2f(m - m_cand);
-        if (EMPTY_ROWS && m_cand == -INFINITY) alpha = 1.0f;
-        m = m_cand;
-    }
-    return alpha;
+    if (__builtin_amdgcn_ballot_w64(m_cand - m > kRescaleThreshold) == 0) return;
+    float alpha = __builtin_amdgcn_exp2f(m - m_cand);
+    if (EMPTY_ROWS && m_cand == -INFINITY) alpha = 1.0f;
+    m = m_cand;
+    lpart *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+        acc_o[t] *= alpha;
 }
 
 // The max the probabilities are taken against: a row that has seen no visible
@@ -323,15 +339,6 @@ __device__ __forceinline__ void accumulate_pv(const LDS_AS char *vb, const typen
         }
 }
 
-template <int D>
-__device__ __forceinline__ void rescale(f32x16 (&acc_o)[D / 32], float &lpart, float alpha)
-{
-    lpart *= alpha;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t)
-        acc_o[t] *= alpha;
-}
-
 // One step of the pipelined loop for tile j: probabilities of tile j (VALU)
 // while the scores of tile j+1 run (MFMA), then O~ += P~_j V_j (MFMA) while the
 // max of tile j+1 is taken (VALU).  Where kLateTileLoads<D>, the step issues the
@@ -341,12 +348,11 @@ template <int D, typename E, bool CAUSAL, bool EMPTY_ROWS, bool WINDOW, bool DRO
           typename Loads = NoTileLoads>
 __device__ __forceinline__ void pipelined_step(Loads &&late_loads, const LDS_AS char *k_next, const LDS_AS char *v_cur,
                                                const typename V16<E>::x8 (&qf)[D / 16], f32x16 (&acc_o)[D / 32],
-                                               f32x16 (&s_cur)[2], float &m, float &lpart, float &alpha,
+                                               f32x16 (&s_cur)[2], float &m, float &lpart,
                                                float c2, int j, int t0, int plain_lo, int n_plain, int Lk,
                                                int qrow, int hh, int k_lane, int v_lane, int wl, int wr,
                                                const DropoutParams &dp, int lane, int bh)
 {
-    if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
     typename V16<E>::x8 pf[4];
     const DropMask mk = tile_mask<DROPOUT>(dp, (t0 + j) * kBc, qrow, lane, bh);
     const float rs = probabilities<E, DROPOUT>(s_cur, c2, reference_max<EMPTY_ROWS>(m), pf, mk, dp.threshold);
@@ -366,7 +372,7 @@ __device__ __forceinline__ void pipelined_step(Loads &&late_loads, const LDS_AS 
         mask_scores<CAUSAL, WINDOW>(s_next, (t0 + j + 1) * kBc, Lk, qrow, hh, wl, wr);
         mt = row_max_scaled(s_next, c2);
     }
-    alpha = update_max<EMPTY_ROWS>(m, mt);
+    update_max<D, EMPTY_ROWS>(m, mt, acc_o, lpart);
     s_cur[0] = s_next[0];
     s_cur[1] = s_next[1];
 }
@@ -521,7 +527,6 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         acc_o[t] = f32x16{};
     float m = -INFINITY;     // reference max (base-2 units), per query row
     float lpart = 0.f;       // running sum over this lane's half of the keys
-    float alpha = 1.f;       // pending rescale of O~ and l
     const float c2 = p.scale_log2;
 
     __builtin_amdgcn_s_waitcnt(0);
@@ -548,7 +553,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
                 load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
             };
             pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(loads_even,
-                (const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+                (const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur, m, lpart, c2, j, t0,
                 plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -558,7 +563,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
                 load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
             };
             pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(loads_odd,
-                (const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+                (const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur, m, lpart, c2, j, t0,
                 plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -570,7 +575,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK0, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV1, wave, loff);
         pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(NoTileLoads{},
-            (const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+            (const LDS_AS char *)sK1, (const LDS_AS char *)sV0, qf, acc_o, s_cur, m, lpart, c2, j, t0,
             plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
         __builtin_amdgcn_s_waitcnt(0);        // this wave's loads have landed
         __syncthreads();                      // ... everyone's, and the read buffers are free
@@ -579,7 +584,7 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, sK1, wave, loff);
         load_tile_async<D, true>(rV, t0 + j + 1, sV0, wave, loff);
         pipelined_step<D, E, CAUSAL, kEmptyRows, WINDOW, DROPOUT>(NoTileLoads{},
-            (const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur, m, lpart, alpha, c2, j, t0,
+            (const LDS_AS char *)sK0, (const LDS_AS char *)sV1, qf, acc_o, s_cur, m, lpart, c2, j, t0,
             plain_lo, n_plain, p.Lk, qrow, hh, k_lane, v_lane, p.wl, p.wr, p.drop, lane, bh);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -590,7 +595,6 @@ void fa2_fwd_bf16_kernel(FwdParams p)
         const bool odd = j & 1;
         if (j + 2 < n_kv) load_tile_async<D, false>(rK, t0 + j + 2, odd ? sK1 : sK0, wave, loff);
         if (j + 1 < n_kv) load_tile_async<D, true>(rV, t0 + j + 1, odd ? sV0 : sV1, wave, loff);
-        if (alpha != 1.0f) rescale<D>(acc_o, lpart, alpha);
         e8 pf[4];
         const DropMask mk = tile_mask<DROPOUT>(p.drop, (t0 + j) * kBc, qrow, lane, bh);
         lpart += probabilities<E, DROPOUT>(s_cur, c2, reference_max<kEmptyRows>(m), pf, mk, p.drop.threshold);
