@@ -11,15 +11,16 @@ and the stream.
 import math
 
 from . import _lib
-from ._lib import (FA2_MAX_SPLITS, FA2Error, fa2_bwd, fa2_bwd_dropout, fa2_bwd_dropout_f16,  # noqa: F401
-                   fa2_bwd_f16, fa2_bwd_window, fa2_bwd_window_f16, fa2_bwd_workspace_bytes, fa2_check_args,
-                   fa2_fwd, fa2_fwd_dropout, fa2_fwd_dropout_f16, fa2_fwd_f16, fa2_fwd_f32, fa2_fwd_splitkv,
-                   fa2_fwd_splitkv_f16, fa2_fwd_window, fa2_fwd_window_f16, fa2_merge_partials,
-                   fa2_merge_partials_f16, fa2_splitkv_num_splits, fa2_splitkv_workspace_bytes, lib,
-                   status_string)
+from ._lib import (FA2_MAX_SPLITS, FA2_STATIC_SCRATCH_BYTES, FA2Error, fa2_bwd, fa2_bwd_dropout,  # noqa: F401
+                   fa2_bwd_dropout_f16, fa2_bwd_f16, fa2_bwd_window, fa2_bwd_window_f16, fa2_bwd_workspace_bytes,
+                   fa2_check_args, fa2_fwd, fa2_fwd_dropout, fa2_fwd_dropout_f16, fa2_fwd_f16, fa2_fwd_f32,
+                   fa2_fwd_splitkv, fa2_fwd_splitkv_f16, fa2_fwd_splitkv_static, fa2_fwd_window,
+                   fa2_fwd_window_f16, fa2_merge_partials, fa2_merge_partials_f16, fa2_splitkv_num_splits,
+                   fa2_splitkv_workspace_bytes, lib, status_string)
 
 __all__ = ["forward", "backward", "merge_partials", "FA2Error", "status_string", "FA2_MAX_SPLITS",
-           "fa2_check_args", "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits", "fa2_bwd_workspace_bytes"] + \
+           "FA2_STATIC_SCRATCH_BYTES", "fa2_check_args", "fa2_splitkv_workspace_bytes", "fa2_splitkv_num_splits",
+           "fa2_bwd_workspace_bytes"] + \
     sorted(n for n in _lib.SIGNATURES if n.startswith("fa2_") and n not in ("fa2_status_string",))
 
 

@@ -13,9 +13,10 @@ FA2_OK = 0
 STATUS_NAMES = {
     0: "FA2_OK", 1: "FA2_ERR_NULL", 2: "FA2_ERR_DIM", 3: "FA2_ERR_UNSUPPORTED_D",
     4: "FA2_ERR_ARG", 5: "FA2_ERR_ALIGN", 6: "FA2_ERR_DEVICE", 7: "FA2_ERR_LAUNCH",
-    8: "FA2_ERR_WORKSPACE",
+    8: "FA2_ERR_WORKSPACE", 9: "FA2_ERR_SCRATCH",
 }
 FA2_MAX_SPLITS = 128
+FA2_STATIC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 # name -> (restype, argtypes), exactly the declarations of include/fa2.h
 _P = ctypes.c_void_p
@@ -33,6 +34,7 @@ SIGNATURES = {
     "fa2_status_string": (ctypes.c_char_p, [_I]),
     "fa2_check_args": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I]),
     "fa2_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P, _Z, _P]),
+    "fa2_fwd_splitkv_static": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa2_splitkv_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "fa2_splitkv_num_splits": (_I, [_I, _I, _I, _I, _I, _I]),
     "fa2_merge_partials": (_I, [_P, _P, _I, _L, _I, _P, _P, _P]),
@@ -144,6 +146,11 @@ def fa2_fwd_splitkv_f16(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_spl
     """``fa2_fwd_splitkv_f16`` (fp16)."""
     _call("fa2_fwd_splitkv_f16", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, workspace,
           workspace_bytes, stream)
+
+
+def fa2_fwd_splitkv_static(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, stream):
+    """``fa2_fwd_splitkv_static`` (bf16 split K/V + merge, partials in the library's static scratch)."""
+    _call("fa2_fwd_splitkv_static", q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, num_splits, stream)
 
 
 def fa2_merge_partials(o_parts, lse_parts, n_parts, rows, d, o, lse, stream):

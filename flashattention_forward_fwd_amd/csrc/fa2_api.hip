@@ -285,6 +285,50 @@ int fwd_dropout16(const void *q, const void *k, const void *v, void *o, float *l
     return FA2_OK;
 }
 
+// Launches the split-KV forward for S >= 1 ranges with the partial results in
+// `workspace` (big enough for S; unused when S == 1): the partial kernel (or the
+// decoding kernel for a few query rows), then the merge.
+int splitkv_launch(const fa2::FwdParams &p, int S, int d, int causal, bool f16, void *workspace, void *o,
+                   float *lse, hipStream_t s)
+{
+    if (S == 1) {                             // one range: the one-pass kernel
+        if (fa2::launch_fwd16(p, d, causal != 0, f16, fa2::FwdVariant::kPlain, s) != hipSuccess)
+            return FA2_ERR_LAUNCH;
+        return FA2_OK;
+    }
+    const int64_t rows = (int64_t)p.B * p.H * p.Lq;
+    float *o_parts = static_cast<float *>(workspace);
+    float *lse_parts = reinterpret_cast<float *>(static_cast<char *>(workspace) + partial_o_bytes(S, rows, d));
+    fa2::FwdParams pp = p;
+    pp.o = o_parts;
+    pp.lse = lse_parts;
+    pp.n_splits = S;
+    if (p.Lq <= fa2::kDecodeMaxRows) {        // a few query rows: the decoding kernel
+        pp.n_wg = p.B * p.H * S;
+        if (fa2::launch_decode(pp, d, f16, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    } else {
+        pp.n_wg = p.n_wg * S;
+        if (fa2::launch_fwd16(pp, d, causal != 0, f16, fa2::FwdVariant::kSplit, s) != hipSuccess)
+            return FA2_ERR_LAUNCH;
+    }
+    if (fa2::launch_merge(o_parts, lse_parts, S, rows, d, f16, o, lse, s) != hipSuccess) return FA2_ERR_LAUNCH;
+    return FA2_OK;
+}
+
+// Range count of a split-KV call and the partial-result bytes it needs; the
+// status of the size checks.  num_splits == 0 asks the device (auto_splits).
+int splitkv_size(const fa2::FwdParams &p, int num_splits, int d, int causal, int *S_out, size_t *need_out)
+{
+    const int S = num_splits == 0 ? auto_splits(p.B, p.H, p.Lq, p.Lk, causal) : num_splits;
+    if ((int64_t)p.n_wg * S > INT32_MAX) return FA2_ERR_DIM;
+    if (!merge_grid_fits((int64_t)p.B * p.H * p.Lq, d)) return FA2_ERR_DIM;
+    const size_t need = workspace_bytes(S, p.B, p.H, p.Lq, d);
+    if (need == 0) return FA2_ERR_DIM;
+    *S_out = S;
+    *need_out = need;
+    return FA2_OK;
+}
+
 int fwd_splitkv16(const void *q, const void *k, const void *v, void *o, float *lse, int B, int H, int Lq, int Lk,
                   int d, float scale, int causal, int num_splits, void *workspace, size_t workspace_bytes_given,
                   bool f16, void *stream)
@@ -296,36 +340,34 @@ int fwd_splitkv16(const void *q, const void *k, const void *v, void *o, float *l
     if (!workspace) return FA2_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA2_ERR_ALIGN;
     if ((st = check_device()) != FA2_OK) return st;
-    const int S = num_splits == 0 ? auto_splits(B, H, Lq, Lk, causal) : num_splits;
-    if ((int64_t)p.n_wg * S > INT32_MAX) return FA2_ERR_DIM;
-    const int64_t rows = (int64_t)B * H * Lq;
-    if (!merge_grid_fits(rows, d)) return FA2_ERR_DIM;
-    const size_t need = workspace_bytes(S, B, H, Lq, d);
-    if (need == 0) return FA2_ERR_DIM;
+    int S = 0;
+    size_t need = 0;
+    if ((st = splitkv_size(p, num_splits, d, causal, &S, &need)) != FA2_OK) return st;
     if (workspace_bytes_given < need) return FA2_ERR_WORKSPACE;
+    return splitkv_launch(p, S, d, causal, f16, workspace, o, lse, static_cast<hipStream_t>(stream));
+}
 
-    float *o_parts = static_cast<float *>(workspace);
-    float *lse_parts = reinterpret_cast<float *>(static_cast<char *>(workspace) + partial_o_bytes(S, rows, d));
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (S == 1) {                             // one range: the one-pass kernel
-        if (fa2::launch_fwd16(p, d, causal != 0, f16, fa2::FwdVariant::kPlain, s) != hipSuccess)
-            return FA2_ERR_LAUNCH;
-        return FA2_OK;
-    }
-    fa2::FwdParams pp = p;
-    pp.o = o_parts;
-    pp.lse = lse_parts;
-    pp.n_splits = S;
-    if (Lq <= fa2::kDecodeMaxRows) {          // a few query rows: the decoding kernel
-        pp.n_wg = B * H * S;
-        if (fa2::launch_decode(pp, d, f16, s) != hipSuccess) return FA2_ERR_LAUNCH;
-    } else {
-        pp.n_wg = p.n_wg * S;
-        if (fa2::launch_fwd16(pp, d, causal != 0, f16, fa2::FwdVariant::kSplit, s) != hipSuccess)
-            return FA2_ERR_LAUNCH;
-    }
-    if (fa2::launch_merge(o_parts, lse_parts, S, rows, d, f16, o, lse, s) != hipSuccess) return FA2_ERR_LAUNCH;
-    return FA2_OK;
+// ---- fa2_fwd_splitkv_static: the partial results in a static device array
+
+// Device memory of the library, one copy on every device it runs on (held
+// until the process ends).  Host code never uses this name as an address: the
+// host-side symbol is a stand-in, and a kernel given it would fault.  Each
+// device's own address comes from hipGetSymbolAddress (scratch_on_device).
+static __device__ __align__(256) char scratch[FA2_STATIC_SCRATCH_BYTES];
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`: looked up once per device (with
+// that device current) and kept; NULL if the lookup fails.
+void *scratch_on_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    return ptr;
 }
 
 int merge16(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows, int d, void *o, float *lse,
@@ -457,6 +499,27 @@ size_t fa2_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int caus
     return workspace_bytes(S, B, H, Lq, d);
 }
 
+int fa2_fwd_splitkv_static(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int Lq, int Lk, int d, float scale, int causal, int num_splits, void *stream)
+{
+    fa2::FwdParams p;
+    int st = prepare(q, k, v, o, lse, B, H, Lq, Lk, d, scale, causal, 2, &p, kDims16);
+    if (st != FA2_OK) return st;
+    if (num_splits < 0 || num_splits > FA2_MAX_SPLITS) return FA2_ERR_ARG;
+    int S = 0;
+    size_t need = 0;
+    if (num_splits > 0) {                     // sizes known: reject before any HIP call
+        if ((st = splitkv_size(p, num_splits, d, causal, &S, &need)) != FA2_OK) return st;
+        if (S > 1 && need > (size_t)FA2_STATIC_SCRATCH_BYTES) return FA2_ERR_SCRATCH;
+    }
+    if ((st = check_device()) != FA2_OK) return st;
+    if ((st = splitkv_size(p, num_splits, d, causal, &S, &need)) != FA2_OK) return st;
+    if (S > 1 && need > (size_t)FA2_STATIC_SCRATCH_BYTES) return FA2_ERR_SCRATCH;
+    void *ws = S > 1 ? scratch_on_device() : nullptr;
+    if (S > 1 && !ws) return FA2_ERR_DEVICE;
+    return splitkv_launch(p, S, d, causal, false, ws, o, lse, static_cast<hipStream_t>(stream));
+}
+
 int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
                     int num_splits, void *workspace, size_t workspace_bytes_given, void *stream)
@@ -560,6 +623,9 @@ const char *fa2_status_string(int status)
     case FA2_ERR_DEVICE: return "no usable gfx950 HIP device";
     case FA2_ERR_LAUNCH: return "kernel launch failed";
     case FA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA2_ERR_SCRATCH:
+        return "the split-KV partial results need more than the library's static scratch "
+               "(FA2_STATIC_SCRATCH_BYTES); use fa2_fwd_splitkv with a workspace";
     default: return "unknown status";
     }
 }

@@ -74,8 +74,10 @@ typedef enum fa2_status {
     FA2_ERR_ALIGN = 5,           /* a tensor pointer is not 16-byte aligned */
     FA2_ERR_DEVICE = 6,          /* no usable HIP device, or the device is not gfx950 */
     FA2_ERR_LAUNCH = 7,          /* the kernel launch was refused by the runtime */
-    FA2_ERR_WORKSPACE = 8        /* workspace NULL or smaller than fa2_splitkv_workspace_bytes /
+    FA2_ERR_WORKSPACE = 8,       /* workspace NULL or smaller than fa2_splitkv_workspace_bytes /
                                     fa2_bwd_workspace_bytes */
+    FA2_ERR_SCRATCH = 9          /* fa2_fwd_splitkv_static: the partial results need more than
+                                    FA2_STATIC_SCRATCH_BYTES */
 } fa2_status;
 
 /*
@@ -196,6 +198,30 @@ int fa2_fwd_dropout_f16(const void *q, const void *k, const void *v, void *o, fl
 int fa2_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
                     int num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa2_fwd_splitkv without a workspace and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  The partial results live in
+ * a static device array of the library, FA2_STATIC_SCRATCH_BYTES bytes on every
+ * device the library runs on, held until the process ends (its address on a
+ * device is looked up on the first call there).  bf16 only; the same kernels,
+ * split count, results and errors as fa2_fwd_splitkv, plus:
+ *   FA2_ERR_SCRATCH : the partials (fa2_splitkv_workspace_bytes for the same
+ *                     arguments) exceed FA2_STATIC_SCRATCH_BYTES; nothing is
+ *                     launched.  With num_splits > 0 this is decided before any
+ *                     HIP call.  A split count of 1 needs no scratch.
+ * All calls on one device share that device's array and nothing else orders
+ * them: calls that overlap in time on one device (two streams, two host
+ * threads) race on it and may return wrong results.  Serialise them, or use
+ * fa2_fwd_splitkv with a workspace per stream.  The array needs no clearing: a
+ * call writes every partial it reads.
+ */
+#define FA2_STATIC_SCRATCH_BYTES (32u * 1024u * 1024u)
+
+int fa2_fwd_splitkv_static(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int H, int Lq, int Lk, int d, float scale, int causal, int num_splits,
+                           void *stream);
 
 /* fa2_fwd_splitkv on fp16 q, k, v, o (the same workspace; o rounded to fp16, nearest
  * even, by the merge). */

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
                                          "fa2_bwd_window", "fa2_bwd_f16", "fa2_fwd_dropout",
                                          "fa2_bwd_dropout", "fa2_fwd_window_f16", "fa2_fwd_dropout_f16",
                                          "fa2_fwd_splitkv_f16", "fa2_merge_partials_f16",
-                                         "fa2_bwd_window_f16", "fa2_bwd_dropout_f16"])
+                                         "fa2_bwd_window_f16", "fa2_bwd_dropout_f16", "fa2_fwd_splitkv_static"])
 
 
 def test_f16_twins_reject_like_their_bf16_entry_points():
@@ -50,8 +50,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(9):
-        assert fa.status_string(code)
+    for code in range(10):
+        assert fa.status_string(code) != "unknown status"
     assert fa.status_string(99) == "unknown status"
 
 
