@@ -81,7 +81,12 @@ typedef enum fa2_status {
 } fa2_status;
 
 /*
- * Forward pass with bfloat16 q, k, v, o.  Products run on bf16 matrix cores with
+ * Forward pass with bfloat16 q, k, v, o: the operation of "Triton内核实战：手写
+ * FlashAttention-2，优化长序列GPU内存瓶颈", section "标准注意力为何是内存瓶颈" (O =
+ * softmax(Q K^T scale) V), with the host interface of its section "Host端包装器与内核
+ * 启动" (Q, K, V, causal in; O and the per-row statistic out), computed by the
+ * recurrence of "FlashAttention 怎么做? online softmax 怎么更新?", section "推导 / 关键
+ * 公式".  Products run on bf16 matrix cores with
  * fp32 accumulation; the running max m, running sum l and the unnormalised output
  * stay fp32; the probabilities are rounded to bf16 (round to nearest even) before
  * they multiply V; o is rounded to bf16 with round to nearest even; lse is fp32.
@@ -97,15 +102,17 @@ int fa2_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 /*
  * Forward pass with fp16 (IEEE half) q, k, v, o: the same kernel on fp16 matrix
  * cores, probabilities rounded to fp16 and o stored in fp16, both round to
- * nearest even (the fp16 store of the Triton page's kernel, section
- * "流式注意力核心内核").  Same arguments and rules as fa2_fwd.
+ * nearest even (the fp16 store of "Triton内核实战：手写FlashAttention-2，优化长序列GPU
+ * 内存瓶颈", section "流式注意力核心内核").  Same arguments and rules as fa2_fwd.
  */
 int fa2_fwd_f16(const void *q, const void *k, const void *v, void *o, float *lse,
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream);
 
 /*
  * Forward pass with fp32 q, k, v, o: fp32 matrix-core products and fp32 state
- * throughout (no reduced-precision step).  Same arguments and rules as fa2_fwd.
+ * throughout (no reduced-precision step).  The operation of fa2_fwd, i.e. the
+ * attention of "Triton内核实战：手写FlashAttention-2，优化长序列GPU内存瓶颈", section
+ * "标准注意力为何是内存瓶颈", on fp32 inputs.  Same arguments and rules as fa2_fwd.
  */
 int fa2_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                 int B, int H, int Lq, int Lk, int d, float scale, int causal, void *stream);
@@ -128,7 +135,8 @@ int fa2_fwd_window(const void *q, const void *k, const void *v, void *o, float *
                    int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
                    void *stream);
 
-/* fa2_fwd_window on fp16 q, k, v, o (precision as fa2_fwd_f16). */
+/* fa2_fwd_window on fp16 q, k, v, o (precision as fa2_fwd_f16): the window variant of
+ * "Flash Attention 全解析（上）", section 5.3. */
 int fa2_fwd_window_f16(const void *q, const void *k, const void *v, void *o, float *lse,
                        int B, int H, int Lq, int Lk, int d, float scale, int window_left, int window_right,
                        void *stream);
@@ -155,7 +163,8 @@ int fa2_fwd_dropout(const void *q, const void *k, const void *v, void *o, float 
                     int B, int H, int Lq, int Lk, int d, float scale, int causal,
                     double dropout_p, uint64_t seed, uint32_t offset, void *stream);
 
-/* fa2_fwd_dropout on fp16 q, k, v, o (the same keep mask; precision as fa2_fwd_f16). */
+/* fa2_fwd_dropout on fp16 q, k, v, o (the same keep mask; precision as fa2_fwd_f16): the
+ * fused dropout of "Flash Attention 全解析（上）", section 2.1.2. */
 int fa2_fwd_dropout_f16(const void *q, const void *k, const void *v, void *o, float *lse,
                         int B, int H, int Lq, int Lk, int d, float scale, int causal,
                         double dropout_p, uint64_t seed, uint32_t offset, void *stream);
@@ -224,13 +233,16 @@ int fa2_fwd_splitkv_static(const void *q, const void *k, const void *v, void *o,
                            void *stream);
 
 /* fa2_fwd_splitkv on fp16 q, k, v, o (the same workspace; o rounded to fp16, nearest
- * even, by the merge). */
+ * even, by the merge): the split-KV forward of "Flash Attention 全解析（上）", section
+ * 4.3. */
 int fa2_fwd_splitkv_f16(const void *q, const void *k, const void *v, void *o, float *lse,
                         int B, int H, int Lq, int Lk, int d, float scale, int causal,
                         int num_splits, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Workspace bytes fa2_fwd_splitkv needs for these sizes: num_splits * B * H * Lq
+ * Workspace bytes fa2_fwd_splitkv needs for the per-range partial results of the
+ * split-KV forward ("Flash Attention 全解析（上）", section 4.3) for these sizes:
+ * num_splits * B * H * Lq
  * rows of (d + 1) fp32 values, laid out as the partial outputs
  * [num_splits, B, H, Lq, d] followed (at a 256-byte boundary) by the partial
  * logsumexps [num_splits, B, H, Lq].  num_splits == 0 resolves as in
@@ -240,7 +252,9 @@ int fa2_fwd_splitkv_f16(const void *q, const void *k, const void *v, void *o, fl
 size_t fa2_splitkv_workspace_bytes(int B, int H, int Lq, int Lk, int d, int causal, int num_splits);
 
 /*
- * The split count num_splits == 0 stands for: the fewest ranges that give every
+ * The split count num_splits == 0 stands for (the split of the K/V sequence that
+ * fills the device when Q is short, "Flash Attention 全解析（上）", sections 4.1 and
+ * 4.3): the fewest ranges that give every
  * compute unit of the current device one (Q block, range) work-group, or two
  * when causal (Q blocks then differ in length), with at least 8 K/V blocks per
  * range and at most FA2_MAX_SPLITS ranges; 1 when the Q blocks alone fill the
@@ -271,7 +285,9 @@ int fa2_splitkv_num_splits(int B, int H, int Lq, int Lk, int d, int causal);
 int fa2_merge_partials(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                        int d, void *o, float *lse, void *stream);
 
-/* fa2_merge_partials writing fp16 o (round to nearest even). */
+/* fa2_merge_partials writing fp16 o (round to nearest even): the combine of
+ * "FlashAttention 怎么做? online softmax 怎么更新?", follow-up question "多卡(ring
+ * attention)怎么合并两段结果?". */
 int fa2_merge_partials_f16(const float *o_parts, const float *lse_parts, int n_parts, int64_t rows,
                            int d, void *o, float *lse, void *stream);
 
@@ -310,8 +326,9 @@ int fa2_bwd(const void *q, const void *k, const void *v, const void *o, const fl
 
 /*
  * Backward pass of fa2_fwd_f16: fp16 q, k, v, o, dout, dq, dk, dv (fp16 matrix
- * cores, P and dS rounded to fp16, outputs fp16, round to nearest even).  Same
- * arguments and rules as fa2_bwd.
+ * cores, P and dS rounded to fp16, outputs fp16, round to nearest even); the
+ * recomputation of "FlashAttention 怎么做? online softmax 怎么更新?", section
+ * "Recomputation".  Same arguments and rules as fa2_bwd.
  */
 int fa2_bwd_f16(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
                 void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale, int causal,
@@ -324,7 +341,10 @@ int fa2_bwd_f16(const void *q, const void *k, const void *v, const void *o, cons
  * A = P * Z * 256 / t:
  *     dv = A^T dout,   dP = (dout v^T) * Z * 256 / t,   D = rowsum(dout * o),
  *     dS = P * (dP - D),   dq = scale dS k,   dk = scale dS^T q
- * (the derivative of that forward; the reading is described at fa2_fwd_dropout).
+ * (the derivative of that forward; the reading is described at fa2_fwd_dropout;
+ * dropout fused into the pass over a score block as in "Flash Attention 全解析（上）",
+ * section 2.1.2, the probabilities rebuilt as in "FlashAttention 怎么做? online
+ * softmax 怎么更新?", section "Recomputation").
  * Same arguments, precision, workspace and error rules as fa2_bwd; FA2_ERR_ARG
  * also for dropout_p outside [0, 1).
  */
@@ -333,14 +353,17 @@ int fa2_bwd_dropout(const void *q, const void *k, const void *v, const void *o, 
                     double dropout_p, uint64_t seed, uint32_t offset, void *workspace, size_t workspace_bytes,
                     void *stream);
 
-/* fa2_bwd_dropout on fp16 data (the backward of fa2_fwd_dropout_f16). */
+/* fa2_bwd_dropout on fp16 data (the backward of fa2_fwd_dropout_f16; dropout as in
+ * "Flash Attention 全解析（上）", section 2.1.2). */
 int fa2_bwd_dropout_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
                         const void *dout, void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d,
                         float scale, int causal, double dropout_p, uint64_t seed, uint32_t offset,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Backward pass of fa2_fwd_window: the gradients of attention over the key
+ * Backward pass of fa2_fwd_window (the window of "Flash Attention 全解析（上）",
+ * section 5.3, with the recomputation of "FlashAttention 怎么做? online softmax 怎么
+ * 更新?", section "Recomputation"): the gradients of attention over the key
  * window (window_left, window_right) of fa2_fwd_window, from its o and lse.
  * Rows that see no key contribute nothing (their o = 0, D = 0, P = 0); keys no
  * row sees get dk = dv = 0.  Same arguments and rules as fa2_bwd otherwise.
@@ -349,24 +372,32 @@ int fa2_bwd_window(const void *q, const void *k, const void *v, const void *o, c
                    void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d, float scale,
                    int window_left, int window_right, void *workspace, size_t workspace_bytes, void *stream);
 
-/* fa2_bwd_window on fp16 data (the backward of fa2_fwd_window_f16). */
+/* fa2_bwd_window on fp16 data (the backward of fa2_fwd_window_f16; "Flash Attention
+ * 全解析（上）", section 5.3). */
 int fa2_bwd_window_f16(const void *q, const void *k, const void *v, const void *o, const float *lse,
                        const void *dout, void *dq, void *dk, void *dv, int B, int H, int Lq, int Lk, int d,
                        float scale, int window_left, int window_right, void *workspace,
                        size_t workspace_bytes, void *stream);
 
 /*
- * Workspace bytes fa2_bwd needs: lse * log2(e) for the B*H*Lq query rows and,
+ * Workspace bytes fa2_bwd needs for the per-row statistics its recomputation reads
+ * ("FlashAttention 怎么做? online softmax 怎么更新?", section "Recomputation": the
+ * saved L, and D = rowsum(dO * O)): lse * log2(e) for the B*H*Lq query rows and,
  * from the next 256-byte boundary, D = rowsum(dout * o) for the same rows, both
  * fp32.  Returns 0 for sizes that do not fit.
  */
 size_t fa2_bwd_workspace_bytes(int B, int H, int Lq);
 
-/* Static English text for a status code (never NULL). */
+/* Static English text for a status code (never NULL): the status of the argument
+ * checks and launches of the entry points, whose interface is the host wrapper of
+ * "Triton内核实战：手写FlashAttention-2，优化长序列GPU内存瓶颈", section "Host端包装器与
+ * 内核启动". */
 const char *fa2_status_string(int status);
 
 /*
- * Validate arguments exactly as fa2_fwd / fa2_fwd_f16 / fa2_fwd_f32 do, without any
+ * Validate arguments of the forward of "Triton内核实战：手写FlashAttention-2，优化长序列
+ * GPU内存瓶颈" (section "Host端包装器与内核启动") exactly as fa2_fwd / fa2_fwd_f16 /
+ * fa2_fwd_f32 do, without any
  * HIP call.  elem_bytes is 2 (bf16 or fp16) or 4 (fp32).  Returns the status those
  * entry points would return before launching.
  */

@@ -30,6 +30,33 @@ def test_header_declares_the_entry_points():
                                          "fa2_bwd_window_f16", "fa2_bwd_dropout_f16", "fa2_fwd_splitkv_static"])
 
 
+PAGE_TITLES = ("Flash Attention 全解析", "FlashAttention 怎么做", "Triton内核实战",
+               "FlashAttention-2 算法架构升级", "新年一定要学会FlashAttention")
+
+
+def declaration_comments():
+    """(name, comment block just before the declaration) for every function in the header."""
+    text = open(HEADER).read()
+    pat = r"(/\*(?:(?!\*/).)*\*/)\s*(?:#define[^\n]*\n\s*)*(?:int|size_t|const char \*)\s*(fa2_\w+)\s*\("
+    out = []
+    for m in re.finditer(pat, text, flags=re.S):
+        body = re.sub(r"\s*\n\s*\*\s*", " ", m.group(1))      # join comment lines
+        out.append((m.group(2), body))
+    return out
+
+
+def test_every_declaration_cites_a_page():
+    """Each entry point's comment names the page (by title) that defines what it
+    computes; the no-allocation variant names the callers it is for instead."""
+    blocks = dict(declaration_comments())
+    assert sorted(blocks) == header_functions()
+    for name, body in blocks.items():
+        if name == "fa2_fwd_splitkv_static":
+            assert "cannot allocate" in body
+            continue
+        assert any(t in body for t in PAGE_TITLES), name
+
+
 def test_f16_twins_reject_like_their_bf16_entry_points():
     L = fa.lib()
     big = 1 << 30
