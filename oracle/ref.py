@@ -11,10 +11,10 @@ Three references, each a plain reading of the pages:
   ``attn_ref.c`` with the whole score row materialised.
 * ``softmax_3pass`` / ``online_softmax`` -- the safe softmax as three passes, and the
   running-max / running-sum recurrence that replaces the first two passes.
-* ``flash_attention2_tiled`` -- the FlashAttention-2 forward algorithm step by step
-  (Q blocks outside, K/V blocks inside, running m and l, unnormalised output, one
-  division at the end, logsumexp), used to show on the CPU that the tiled method
-  reaches the definition's result.
+* ``flash_attention2_tiled`` -- the blockwise forward (Q blocks outside, K/V blocks
+  inside, each block reduced to its own max, sum, normalised output and
+  logsumexp, the blocks folded by the rescaling rule of ``merge_partials``), used
+  to show on the CPU that the blockwise method reaches the definition's result.
 * ``attention_window_f64`` -- the definition restricted to a window of keys around
   each query (sliding-window / local attention), computed by ``attn_window_ref.c``.
 * ``philox4x32_10`` / ``dropout_mask`` / ``attention_dropout_f64`` -- the counter-based
@@ -270,21 +270,24 @@ def online_softmax(x, block=1):
 
 
 def flash_attention2_tiled(q, k, v, scale, causal, Br, Bc):
-    """FlashAttention-2 forward for one head in float64, block by block.
+    """The blockwise forward for one head in float64: Q blocks of Br rows, K/V blocks
+    of Bc rows, no full score row ever formed.
 
     q: [Lq, d]; k, v: [Lk, d].  Returns (o [Lq, d], lse [Lq]).
 
-    Steps, in the order the pages give them:
-      outer loop over Q blocks of Br rows; state m = -inf, l = 0, O~ = 0;
-      inner loop over K/V blocks of Bc rows, ascending, skipping blocks whose
-      every key is masked for every row of the Q block (causal);
-        S = scale * Q_i K_j^T, masked keys set to -inf;
-        m' = max(m, rowmax S);  P~ = exp(S - m');  alpha = exp(m - m');
-        l = alpha * l + rowsum P~;  O~ = diag(alpha) O~ + P~ V_j;  m = m';
-      after the last block: O = O~ / l and lse = m + log(l).
-    "FlashAttention 怎么做? online softmax 怎么更新?" sections "推导 / 关键公式" and
-    "FlashAttention-2 改了什么"; "FlashAttention-2 算法架构升级" sections 一.2 (deferred
-    division) and 二.2 (Q loop outside); "Triton内核实战" section "流式注意力核心内核".
+    Every (Q block, K/V block) pair is first reduced on its own to the block's
+    statistics: its row max m_j, row sum l_j = sum exp(S_j - m_j), its output
+    normalised by that sum, O_j = exp(S_j - m_j) V_j / l_j, and its logsumexp
+    L_j = m_j + log l_j (L_j = -inf for a row that sees no key of the block).  The
+    K/V blocks of a Q block are visited in ascending order, those whose keys are all
+    masked for every row of the Q block are skipped (causal), and their results are
+    folded with ``merge_partials``.  Folding (L, O) pairs is the running-state update
+    of the pages written for normalised parts: multiplying the old sum and output by
+    exp(m_old - m_new) and adding the new block is the same as weighting the two
+    normalised parts by exp(L_part - L_new) ("FlashAttention 怎么做? online softmax
+    怎么更新?", sections "推导 / 关键公式" and "FlashAttention-2 改了什么", and its
+    follow-up "多卡(ring attention)怎么合并两段结果?"; the Q loop outside as in
+    "FlashAttention-2 算法架构升级" section 二.2).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -295,27 +298,23 @@ def flash_attention2_tiled(q, k, v, scale, causal, Br, Bc):
     lse = np.empty(Lq)
     for i0 in range(0, Lq, Br):
         i1 = min(i0 + Br, Lq)
-        Qi = q[i0:i1]
-        rows = np.arange(i0, i1)
-        m = np.full(i1 - i0, -np.inf)
-        l = np.zeros(i1 - i0)
-        Ot = np.zeros((i1 - i0, d))
+        qrow = np.arange(i0, i1)
+        o_parts, l_parts = [], []
         for j0 in range(0, Lk, Bc):
-            if causal and j0 > i1 - 1:
-                break                       # every later block is fully masked
+            if causal and j0 > qrow[-1]:
+                break                       # this block and every later one are masked for all rows
             j1 = min(j0 + Bc, Lk)
-            S = scale * (Qi @ k[j0:j1].T)
+            S = scale * (q[i0:i1] @ k[j0:j1].T)
             if causal:
-                cols = np.arange(j0, j1)
-                S = np.where(cols[None, :] > rows[:, None], -np.inf, S)
-            m_new = np.maximum(m, S.max(axis=1))
-            P = np.exp(S - m_new[:, None])
-            alpha = np.exp(m - m_new)
-            l = alpha * l + P.sum(axis=1)
-            Ot = alpha[:, None] * Ot + P @ v[j0:j1]
-            m = m_new
-        o[i0:i1] = Ot / l[:, None]
-        lse[i0:i1] = m + np.log(l)
+                S = np.where(np.arange(j0, j1)[None, :] > qrow[:, None], -np.inf, S)
+            m_blk = S.max(axis=1)
+            seen = np.isfinite(m_blk)                   # the row sees a key of this block
+            shift = np.where(seen, m_blk, 0.0)
+            E = np.exp(S - shift[:, None])              # exp(-inf) = 0 on masked keys
+            l_blk = np.where(seen, E.sum(axis=1), 1.0)
+            o_parts.append((E @ v[j0:j1]) / l_blk[:, None])
+            l_parts.append(np.where(seen, m_blk + np.log(l_blk), -np.inf))
+        o[i0:i1], lse[i0:i1] = merge_partials(np.stack(o_parts), np.stack(l_parts))
     return o, lse
 
 
