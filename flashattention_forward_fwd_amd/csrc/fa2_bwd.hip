@@ -380,24 +380,38 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
                     for (int h = 0; h < S::kHalves; ++h)
                         mk.y[h] = mask_key_lanes_one(p.drop, t * kRowTile, h, key, lane, bh);
-                e8 pf[S::kPChunks];
+                // P = 2^(S c - lse2), in place.
 #pragma unroll
                 for (int c = 0; c < S::kPChunks; ++c) {
                     const int h = c >> 1, i0 = 8 * (c & 1);
                     const f32x4 l4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 4 * hh);
                     const f32x4 l4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 8 + 4 * hh);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        s[h][i0 + e] = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(s[h][i0 + e], c2, -(e < 4 ? l4a[e] : l4b[e - 4])));
+                }
+                // Pairs outside the window -> 0: one branch per tile, the same on
+                // every lane (a test per entry would split the loop into blocks).
+                if (need_mask) {
+#pragma unroll
+                    for (int h = 0; h < S::kHalves; ++h)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int row = t * kRowTile + 32 * h + 8 * (i / 4) + 4 * hh + (i % 4);
+                            const bool hidden = (p.wl >= 0 && key < row - p.wl) || (p.wr >= 0 && key > row + p.wr);
+                            s[h][i] = hidden ? 0.f : s[h][i];
+                        }
+                }
+                e8 pf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
+                    const int h = c >> 1, i0 = 8 * (c & 1);
                     f32x8 v8;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float l2 = e < 4 ? l4a[e] : l4b[e - 4];
-                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[h][i0 + e], c2, -l2));
-                        if (need_mask) {
-                            const int row = t * kRowTile + 16 * c + 8 * (e / 4) + 4 * hh + (e % 4);
-                            const bool hidden = (p.wl >= 0 && key < row - p.wl) || (p.wr >= 0 && key > row + p.wr);
-                            pv = hidden ? 0.f : pv;
-                        }
-                        v8[e] = pv;
-                        if (DROPOUT && !keep(mk, h, i0 + e, p.drop.threshold)) v8[e] = -pv;
+                        v8[e] = s[h][i0 + e];
+                        if (DROPOUT && !keep(mk, h, i0 + e, p.drop.threshold)) v8[e] = -v8[e];
                     }
                     pf[c] = __builtin_convertvector(v8, e8);
                     pdst[c * kWave + lane] = pf[c];
@@ -473,6 +487,21 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 }
 
 // ---------------------------------------------------------------- 3. dQ
+// Probabilities of one 32-key score tile (keys x this lane's query, first key
+// k0; entry i is key k0 + 8(i/4) + 4hh + i%4) set to 0 where the key is past Lk
+// or (MASKED) outside the window of query qrow.
+template <bool MASKED>
+__device__ __forceinline__ void mask_hidden(f32x16 &pt, int k0, int qrow, int hh, const BwdParams &p)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int kk = k0 + 8 * (i / 4) + 4 * hh + (i % 4);
+        bool hidden = kk >= p.Lk;
+        if (MASKED) hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
+        pt[i] = hidden ? 0.f : pt[i];
+    }
+}
+
 // d = 256: Q, dO and the dQ accumulator take 256 registers, so that instance runs
 // one wavefront per SIMD with the accumulation registers in use (and one
 // work-group per CU: 128 KiB of LDS), as the d = 256 forward.
@@ -592,23 +621,19 @@ void fa2_bwd_dq_kernel(BwdParams p)
                 };
                 // dS / ks of half t (dlt = D / ks, keep bytes y of that half) as the B
                 // operands of key chunks 2t, 2t + 1.
-                auto dscores = [&](int t, const f32x16 &s_t, const f32x16 &dp_t, const u32x4 &y, e8 *dsf) {
+                auto dscores = [&](int t, f32x16 &s_t, const f32x16 &dp_t, const u32x4 &y, e8 *dsf) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s_t[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_t[i], c2, -lse2));
+                    if (need_mask) mask_hidden<MASKED>(s_t, (t0 + j) * kBc + 32 * t, qrow, hh, p);
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         f32x8 ds8;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const int i = 8 * h + e;
-                            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s_t[i], c2, -lse2));
-                            if (need_mask) {
-                                const int kk = (t0 + j) * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
-                                bool hidden = kk >= p.Lk;
-                                if (MASKED)
-                                    hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
-                                pv = hidden ? 0.f : pv;
-                            }
                             const bool kept = ((y[i / 4] >> (8 * (i % 4))) & 0xFFu) < p.drop.threshold;
-                            ds8[e] = pv * (kept ? dp_t[i] - dlt : -dlt);
+                            ds8[e] = s_t[i] * (kept ? dp_t[i] - dlt : -dlt);
                         }
                         dsf[h] = __builtin_convertvector(ds8, e8);
                     }
@@ -644,23 +669,25 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     for (int c = 0; c < kDc; ++c)
                         dp[t] = mfma_32x32x16(read_rows_op<D, E>(vbuf, 32 * t + l32, c, hh), of[c], dp[t]);
                 }
+                // P = 2^(S c - lse2) in place; hidden pairs -> 0 under one branch per
+                // tile (the same on every lane).
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        s[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -lse2));
+                if (need_mask)
+#pragma unroll
+                    for (int t = 0; t < 2; ++t)
+                        mask_hidden<MASKED>(s[t], (t0 + j) * kBc + 32 * t, qrow, hh, p);
                 e8 dsf[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int t = c >> 1, i0 = 8 * (c & 1);
                     f32x8 ds8;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int i = i0 + e;
-                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][i], c2, -lse2));
-                        if (need_mask) {
-                            const int kk = (t0 + j) * kBc + 32 * t + 8 * (i / 4) + 4 * hh + (i % 4);
-                            bool hidden = kk >= p.Lk;
-                            if (MASKED) hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
-                            pv = hidden ? 0.f : pv;
-                        }
-                        ds8[e] = pv * (dp[t][i] - dlt);
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        ds8[e] = s[t][i0 + e] * (dp[t][i0 + e] - dlt);
                     dsf[c] = __builtin_convertvector(ds8, e8);
                 }
                 // dQ^T += K^T dS^T (contraction over the tile's keys).
