@@ -148,14 +148,35 @@ __device__ __forceinline__ typename V16<E>::x8 read_rows_op(const LDS_AS char *t
 // 16c + 8 + 4hh + 0..3 (slots 4-7), hh = l / 32.  Lane 16g + 4e + r supplies the
 // address of row 4(g/2) + e (+16c, +8 for the second read), columns
 // 32 dt + 16(g%2) + 4r .. +3.
-template <int D, typename E>
-__device__ __forceinline__ typename V16<E>::x8 read_cols_op(const LDS_AS char *tile, int dt, int c, int lane)
+//
+// The swizzle depends on the row's low four bits only, so for a d tile dt the
+// reads of chunk c sit 16 c rows past those of chunk 0: ColsOffsets holds the
+// per-lane byte offsets of chunk 0 (rows 4(g/2) + e and that + 8), computed once
+// per wavefront, and read_cols_op adds the compile-time 16 c rows.
+template <int D> struct ColsOffsets {
+    int lo[D / 32], hi[D / 32];
+};
+template <int D>
+__device__ __forceinline__ ColsOffsets<D> cols_offsets(int lane)
 {
     const int g = lane >> 4, e = (lane >> 2) & 3, r = lane & 3;
-    const int row = 16 * c + 4 * (g >> 1) + e;
-    const int x = 2 * (32 * dt + 16 * (g & 1) + 4 * r);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(tile + BTile<D>::addr(row, x)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(tile + BTile<D>::addr(row + 8, x)));
+    const int row = 4 * (g >> 1) + e;
+    ColsOffsets<D> o;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+        const int x = 2 * (32 * dt + 16 * (g & 1) + 4 * r);
+        o.lo[dt] = BTile<D>::addr(row, x);
+        o.hi[dt] = BTile<D>::addr(row + 8, x);
+    }
+    return o;
+}
+template <int D, typename E>
+__device__ __forceinline__ typename V16<E>::x8 read_cols_op(const LDS_AS char *tile, const ColsOffsets<D> &o, int dt,
+                                                            int c)
+{
+    const LDS_AS char *t = tile + 16 * c * BTile<D>::kRowBytes;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(t + o.lo[dt]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4 *)(t + o.hi[dt]));
     return __builtin_bit_cast(typename V16<E>::x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -340,6 +361,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     for (int c = 0; c < kDc; ++c)
         xf[c] = load_row_chunk<E>(Xr + 16 * c + 8 * hh, key < p.Lk);
 
+    const ColsOffsets<D> coff = cols_offsets<D>(lane);
     f32x16 acc[kDt];                       // dV^T (wavefronts 0-3) or dK^T (4-7)
 #pragma unroll
     for (int t = 0; t < kDt; ++t)
@@ -350,9 +372,12 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     __syncthreads();
 
     // Step t: the dV wavefronts work on tile t, the dK wavefronts on tile t - 1.
-    for (int t = t0; t <= t_end; ++t) {
-        if (t + 1 < t_end) load(t + 1);
-        if (!is_dk) {
+    // Each role runs a loop of its own (the same trip count, so the same
+    // barriers): in one shared loop the register allocator kept the accumulator
+    // of the two roles in different registers and copied it on every step.
+    if (!is_dk) {
+        for (int t = t0; t <= t_end; ++t) {
+            if (t + 1 < t_end) load(t + 1);
             if (t >= wt0 && t < wt_end) {
                 const int slot = (t - t0) % 3;
                 const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
@@ -427,9 +452,14 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < S::kPChunks; ++c)
-                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, dt, c, lane), pf[c], acc[dt]);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, coff, dt, c), pf[c], acc[dt]);
             }
-        } else {
+            __builtin_amdgcn_s_waitcnt(0);    // this wave's loads of tile t+1 have landed
+            __syncthreads();                  // ... everyone's; P of tile t is visible; old buffers free
+        }
+    } else {
+        for (int t = t0; t <= t_end; ++t) {
+            if (t + 1 < t_end) load(t + 1);
             const int tk = t - 1;
             if (tk >= wt0 && tk < wt_end) {
                 const int slot = (tk - t0) % 3;
@@ -471,11 +501,11 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < S::kPChunks; ++c)
-                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, dt, c, lane), dsf[c], acc[dt]);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, coff, dt, c), dsf[c], acc[dt]);
             }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
         }
-        __builtin_amdgcn_s_waitcnt(0);        // this wave's loads of tile t+1 have landed
-        __syncthreads();                      // ... everyone's; P of tile t is visible; old buffers free
     }
 
     if (key >= p.Lk) return;
@@ -585,6 +615,7 @@ void fa2_bwd_dq_kernel(BwdParams p)
     }
     const float lse2 = row_ok ? p.lse2[qoff] : 0.f;
     const float dlt = row_ok ? p.delta[qoff] : 0.f;
+    const ColsOffsets<D> coff = cols_offsets<D>(lane);
 
     f32x16 acc[kDt];
 #pragma unroll
@@ -653,7 +684,7 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
-                            acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, dt, 2 * t + h, lane), dsf[h], acc[dt]);
+                            acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, coff, dt, 2 * t + h), dsf[h], acc[dt]);
                 }
             } else {
                 // S^T = K Q^T and dP^T = V dO^T: (keys x this wavefront's queries).
@@ -695,7 +726,7 @@ void fa2_bwd_dq_kernel(BwdParams p)
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, dt, c, lane), dsf[c], acc[dt]);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, coff, dt, c), dsf[c], acc[dt]);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
