@@ -90,12 +90,67 @@ def stored_counters(workload_name):
         return None
     keys = ("mfma_busy_frac", "clock_ghz", "valu_coexec_frac", "valu_insts_per_score_element",
             "trans_insts_per_score_element", "lds_insts_per_wave_tile", "lds_bank_conflict_cycles")
+    optional = ("lds_busy_frac", "wave_wait_any_frac", "wave_wait_issue_frac", "wave_issue_frac",
+                "lds_latency_cycles", "vmem_latency_cycles")
     try:
         out = {k: float(fields[k]) for k in keys}
+        out.update({k: float(fields[k]) for k in optional if k in fields})
     except (KeyError, ValueError):
         return None
     out["source"] = os.path.join("profiles", os.path.basename(COUNTERS_FILE))
     return out
+
+
+def device_peak():
+    """Compute units and peak shader clock of device 0, read through the HIP
+    runtime this process already uses, and the dense bf16 MFMA peak they imply
+    (gfx950: 4096 FLOP per clock per CU).  The roofline's peak stays MI355X's
+    published 2.5 PFLOP/s; this is the cross-check."""
+    import ctypes
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clock_khz = None
+    try:
+        with open("/proc/self/maps") as f:
+            path = next((ln.split()[-1] for ln in f if "libamdhip64.so" in ln), None)
+        if path:
+            hip = ctypes.CDLL(path)
+            val = ctypes.c_int(0)
+            # hipDeviceGetAttribute(&val, hipDeviceAttributeClockRate (5), device 0): kHz
+            if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0 and 100000 < val.value < 10000000:
+                clock_khz = val.value
+    except (OSError, AttributeError):
+        clock_khz = None
+    out = {"cus": cus, "max_sclk_mhz": clock_khz / 1000.0 if clock_khz else None,
+           "bf16_flop_per_clk_per_cu": 4096}
+    out["bf16_peak_tflops"] = round(cus * clock_khz * 1e3 * 4096 / 1e12, 1) if clock_khz else None
+    return out
+
+
+def warm_up(fn, call, stream, min_launches, min_seconds=1.0, max_seconds=10.0, window_ms=20.0):
+    """Untimed launches until at least min_launches have run, at least min_seconds
+    have passed, and the last three windows of about window_ms of GPU work each
+    agree within 0.5 % (max over min): the shader clock of MI355X settles only
+    after about a hundred milliseconds of load (the first launches of a run take
+    ~12 % longer).  Returns (launches, seconds, settled)."""
+    import torch
+    n, per_window, recent = 0, 5, []
+    t0 = time.perf_counter()
+    while True:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(per_window):
+            fn(*call)
+        b.record(stream)
+        torch.cuda.synchronize()
+        n += per_window
+        per_launch = a.elapsed_time(b) / per_window
+        recent = (recent + [per_launch])[-3:]
+        per_window = max(5, int(window_ms / max(per_launch, 1e-3)))
+        dt = time.perf_counter() - t0
+        settled = len(recent) == 3 and max(recent) <= 1.005 * min(recent)
+        if (n >= min_launches and dt >= min_seconds and settled) or dt >= max_seconds:
+            return n, dt, settled
 
 
 def cpu_baseline(w, q, k, v, rows_per_head):
@@ -155,9 +210,8 @@ def calibrate_copy(nbytes):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    # The default warm-up (about 60 ms of kernels on the headline workload) lets
-    # the GPU clock settle: with 10 warm-up steps the first timed steps ran ~13 %
-    # slower on MI355X.
+    # Warm-up: at least --warmup launches, and more until the per-launch time has
+    # settled (see warm_up); the JSON line reports how many ran.
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline causal N=4096, d=128)")
@@ -284,13 +338,13 @@ def main():
         split_info = {"num_splits": S, "requested": args.splits, "workspace_bytes": ws_bytes,
                       "timed_call": "fa2_fwd_splitkv = partial kernel + merge kernel"}
 
-    for _ in range(args.warmup):
-        fn(*call)
-    torch.cuda.synchronize()
-
     K = args.steps
+    # events made before the warm-up, so nothing but a synchronisation separates it
+    # from the timed launches (an idle GPU lowers its clock within milliseconds)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    warm_launches, warm_s, warm_settled = warm_up(fn, call, stream, args.warmup)
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
@@ -304,6 +358,7 @@ def main():
     ms_step = start.elapsed_time(stop) / K
     launch_ms = [a.elapsed_time(b) for a, b in ev]
     avg_launch_ms = sum(launch_ms) / K
+    med_launch_ms = sorted(launch_ms)[K // 2] if K % 2 else 0.5 * sum(sorted(launch_ms)[K // 2 - 1:K // 2 + 1])
 
     flops = flops_override if flops_override is not None else w.flops * (2.5 if bwd_info else 1.0)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -325,11 +380,25 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof.update({"traffic": traffic, "avg_launch_ms": round(avg_launch_ms, 5),
-                 "min_launch_ms": round(min(launch_ms), 5)})
+                 "median_launch_ms": round(med_launch_ms, 5), "min_launch_ms": round(min(launch_ms), 5),
+                 "launch_timing": "HIP events on the launch stream around each of the K timed calls",
+                 "l2_flushed": False,
+                 "l2_note": "no cache flush between calls: consecutive calls find part of Q, K, V in the "
+                            "256 MiB Infinity Cache, as a model running attention back to back would"})
+    # HBM bytes moved per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, committed summary)
+    # over the kernel's average launch time, against the 8 TB/s HBM3E peak.
+    if traffic is not None:
+        roof["hbm_achieved_gbs"] = round(traffic / (avg_launch_ms * 1e-3) / 1e9, 1)
+        roof["hbm_peak_gbs"] = PEAK_HBM_GBS
+        roof["hbm_frac"] = round(roof["hbm_achieved_gbs"] / PEAK_HBM_GBS, 4)
+        roof["traffic_over_algorithmic"] = round(traffic / algo_bytes, 3)
+    if roof["bound"] == "mfma" and w.dtype != "fp32":
+        roof["peak_derivation"] = device_peak()
 
     out = {
         "metric": METRIC_BWD if bwd_info else METRIC, "value": round(value, 2), "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "warmup_launches_run": warm_launches,
+        "warmup_s": round(warm_s, 3), "warmup_settled": warm_settled, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
@@ -341,7 +410,11 @@ def main():
     plain = split_info is None and bwd_info is None and win_info is None and drop_info is None and not args.fp16
     counters = stored_counters(w.name) if plain else None
     if counters is not None:
-        out["counters"] = counters
+        counters["measured_in_this_run"] = False
+        counters["note"] = ("stored: rocprofv3 counters of the same kernel source on this workload, "
+                            "from the committed summary; counter collection serialises dispatches, "
+                            "so they are taken in a run of their own")
+        out["counters_stored"] = counters
     if split_info is not None:
         out["config"]["split_kv"] = split_info
     if args.fp16:
