@@ -232,6 +232,10 @@ def main():
     ap.add_argument("--dropout", type=float, default=None, metavar="P",
                     help="time the dropout entry point (fa2_fwd_dropout, or fa2_bwd_dropout with --backward) "
                          "with drop probability P on a bf16 workload; seed and offset fixed")
+    ap.add_argument("--flush-l2", action="store_true",
+                    help="after the timed steps, time K more calls, each after a read of 512 MiB on the "
+                         "launch stream (evicts the L2s and the 256 MiB Infinity Cache); reported as "
+                         "roofline.l2_flushed_*")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -394,6 +398,35 @@ def main():
         roof["traffic_over_algorithmic"] = round(traffic / algo_bytes, 3)
     if roof["bound"] == "mfma" and w.dtype != "fp32":
         roof["peak_derivation"] = device_peak()
+    if args.flush_l2:
+        # Cold-cache calls: Q, K and V come from HBM, not from the Infinity Cache.  The
+        # flush reads (a sum over a 512 MiB buffer): it leaves clean lines, whose
+        # eviction costs nothing, where a fill would leave dirty ones to write back
+        # during the timed call.
+        flush = torch.zeros(128 << 20, dtype=torch.float32, device="cuda")
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        for _ in range(3):      # the zero fill's dirty lines are written back here, untimed
+            flush.sum()
+            fn(*call)
+        torch.cuda.synchronize()
+        for i in range(K):
+            flush.sum()
+            fev[i][0].record(stream)
+            fn(*call)
+            fev[i][1].record(stream)
+        torch.cuda.synchronize()
+        fms = sorted(a.elapsed_time(b) for a, b in fev)
+        favg = sum(fms) / K
+        roof["l2_flushed_avg_launch_ms"] = round(favg, 5)
+        roof["l2_flushed_median_launch_ms"] = round(fms[K // 2] if K % 2 else 0.5 * (fms[K // 2 - 1] + fms[K // 2]), 5)
+        if roof["bound"] == "mfma":
+            roof["l2_flushed_frac"] = round(flops / (favg * 1e-3) / 1e12 / peak, 4)
+        else:
+            roof["l2_flushed_frac"] = round(algo_bytes / (favg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        roof["l2_flush"] = ("K further calls, each after a read of 512 MiB on the launch stream (more than "
+                            "the 256 MiB Infinity Cache and the eight 4 MiB L2s); value and frac above "
+                            "are the calls without it")
+        del flush
 
     out = {
         "metric": METRIC_BWD if bwd_info else METRIC, "value": round(value, 2), "unit": "TFLOP/s",
