@@ -206,6 +206,23 @@ __device__ __forceinline__ void store_tokens(uint16_t *dst_row, const f32x16 (&a
         }
 }
 
+// Entry i of a 32x32 score accumulator lies at offset 8(i/4) + i%4 (0..27) from
+// the lane's first index `base` (a key or a query row); entries outside [lo, hi]
+// are set to `fill`.  The bounds are brought to entry offsets once per call,
+// clamped to [-1, 64] (an empty range becomes [64, 64]), so each entry costs one
+// unsigned compare and one select.
+__device__ __forceinline__ void keep_range(f32x16 &x, int64_t base, int64_t lo, int64_t hi, float fill)
+{
+    const int64_t a64 = lo - base, b64 = hi - base;
+    int a = (int)(a64 < -1 ? -1 : a64 > 64 ? 64 : a64);
+    int b = (int)(b64 < -1 ? -1 : b64 > 64 ? 64 : b64);
+    if (b < a) a = b = 64;
+    const unsigned span = (unsigned)(b - a);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        x[i] = (unsigned)(8 * (i / 4) + (i % 4) - a) > span ? fill : x[i];
+}
+
 // ---------------------------------------------------------------- 1. prep
 // D_i = sum_t dO_it O_it (fp32) and lse2_i = lse_i * log2(e); D/8 threads per row
 // (a power of two for the butterfly sum: d = 96 takes 16, the last 4 idle).
@@ -419,14 +436,12 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 // Pairs outside the window -> 0: one branch per tile, the same on
                 // every lane (a test per entry would split the loop into blocks).
                 if (need_mask) {
+                    // rows that see this lane's key: [key - wr, key + wl]
+                    const int64_t r_lo = p.wr >= 0 ? (int64_t)key - p.wr : INT64_MIN / 2;
+                    const int64_t r_hi = p.wl >= 0 ? (int64_t)key + p.wl : INT64_MAX / 2;
 #pragma unroll
                     for (int h = 0; h < S::kHalves; ++h)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int row = t * kRowTile + 32 * h + 8 * (i / 4) + 4 * hh + (i % 4);
-                            const bool hidden = (p.wl >= 0 && key < row - p.wl) || (p.wr >= 0 && key > row + p.wr);
-                            s[h][i] = hidden ? 0.f : s[h][i];
-                        }
+                        keep_range(s[h], (int64_t)t * kRowTile + 32 * h + 4 * hh, r_lo, r_hi, 0.f);
                 }
                 e8 pf[S::kPChunks];
 #pragma unroll
@@ -523,13 +538,11 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 template <bool MASKED>
 __device__ __forceinline__ void mask_hidden(f32x16 &pt, int k0, int qrow, int hh, const BwdParams &p)
 {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int kk = k0 + 8 * (i / 4) + 4 * hh + (i % 4);
-        bool hidden = kk >= p.Lk;
-        if (MASKED) hidden = hidden || (p.wl >= 0 && kk < qrow - p.wl) || (p.wr >= 0 && kk > qrow + p.wr);
-        pt[i] = hidden ? 0.f : pt[i];
-    }
+    // keys this lane's query sees: [qrow - wl, qrow + wr] within [0, Lk)
+    int64_t lo = 0, hi = (int64_t)p.Lk - 1;
+    if (MASKED && p.wl >= 0) lo = max(lo, (int64_t)qrow - p.wl);
+    if (MASKED && p.wr >= 0) hi = min(hi, (int64_t)qrow + p.wr);
+    keep_range(pt, (int64_t)k0 + 4 * hh, lo, hi, 0.f);
 }
 
 // d = 256: Q, dO and the dQ accumulator take 256 registers, so that instance runs
