@@ -215,6 +215,9 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline causal N=4096, d=128)")
+    ap.add_argument("--shape", default=None, metavar="B,H,Lq,Lk,d,causal",
+                    help="time another shape instead of a named workload: inputs drawn by the same recipe "
+                         "(bf16, seed 7)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="omit the oracle timing (profiling runs)")
     ap.add_argument("--cpu-rows-per-head", type=int, default=0,
                     help="query rows per (batch, head) for the oracle timing (0: every row)")
@@ -257,7 +260,16 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     fa.lib()   # fail loudly if the HIP library is missing
-    w = dict(WORKLOADS, **DECODE_WORKLOADS)[args.workload or HEADLINE]
+    if args.shape is not None:
+        if args.workload is not None:
+            print("bench.py: --shape replaces --workload", file=sys.stderr)
+            sys.exit(2)
+        from flashattention_forward_fwd_amd.inputs import Workload
+        B, H, Lq, Lk, d, causal = (int(x) for x in args.shape.split(","))
+        name = "B%d_H%d_Lq%d_Lk%d_d%d_bf16%s" % (B, H, Lq, Lk, d, "_causal" if causal else "")
+        w = Workload(name, B, H, Lq, Lk, d, "bf16", bool(causal), 7)
+    else:
+        w = dict(WORKLOADS, **DECODE_WORKLOADS)[args.workload or HEADLINE]
     if args.fp16:
         import dataclasses
         if w.dtype != "bf16":
