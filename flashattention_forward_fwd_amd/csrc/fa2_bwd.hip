@@ -18,7 +18,9 @@
 //     accumulates dV^T, another (V in registers) takes that P through LDS one
 //     step later and accumulates dK^T, while 64-row tiles of Q and dO (and
 //     their D and lse) stream through LDS.  Under the causal mask only the query tiles at
-//     or below the block's first key are visited.
+//     or below the block's first key are visited.  d = 256: 64 keys per
+//     work-group, each accumulator split along d between two wavefronts
+//     (fa2_bwd_dkdv256_kernel), so two wavefronts still share a SIMD.
 //  3. dQ: one work-group per tile of 128 query rows, laid out like the forward
 //     kernel: each wavefront keeps Q and dO of its 32 rows in registers and
 //     accumulates dQ^T while 64-key tiles of K and V stream through LDS.
@@ -269,23 +271,21 @@ __global__ __launch_bounds__(256) void fa2_bwd_prep_kernel(const uint16_t *o, co
 // barrier per step: Q/dO tiles are triple-buffered (t + 1 loading, t read by
 // the dV wavefronts, t - 1 by the dK wavefronts) and P double-buffered.
 //
-// d = 256: a wavefront's K (or V) of 32 keys and its accumulator take 192
-// registers, so the work-group shrinks to four wavefronts (two key groups, 64
-// keys), one per SIMD with the accumulation registers in use, and the Q / dO
-// tiles to 32 rows (the six tiles then take 96 KiB of LDS).
+// d = 256: a wavefront's K (or V) of 32 keys and its accumulator would take 192
+// registers; fa2_bwd_dkdv256_kernel below splits the accumulators along d instead.
 template <int D> struct DkdvShape {
-    static constexpr bool kWide = D == 256;
-    static constexpr int kWaves = kWide ? 4 : 8;              // wavefronts per work-group
+    static_assert(D <= 128, "d = 256 runs fa2_bwd_dkdv256_kernel");
+    static constexpr int kWaves = 8;                           // wavefronts per work-group
     static constexpr int kGroups = kWaves / 2;                 // 32-key groups (one dV, one dK wave each)
     static constexpr int kKeyBlock = kGroups * kKeysPerWave;   // keys per work-group
-    static constexpr int kRowTile = kWide ? 32 : 64;           // query rows per LDS tile
+    static constexpr int kRowTile = 64;                        // query rows per LDS tile
     static constexpr int kHalves = kRowTile / 32;              // 32-row score tiles per row tile
     static constexpr int kPChunks = kRowTile / 16;             // 16-row operand chunks per row tile
     static constexpr int kThreads = kWaves * kWave;
 };
 
 template <int D, bool MASKED, typename E, bool DROPOUT>
-__global__ __launch_bounds__(DkdvShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2, D == 256 ? 1 : 2)))
+__global__ __launch_bounds__(DkdvShape<D>::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa2_bwd_dkdv_kernel(BwdParams p)
 {
     using T = BTile<D>;
@@ -531,6 +531,314 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     else       store_tokens<D, E>(static_cast<uint16_t *>(p.dv) + kv_row * D, acc, DROPOUT ? p.drop.keep_scale : 1.0f, hh);
 }
 
+// d = 256 with two wavefronts per SIMD: the accumulators are split along d.
+// For each group of 32 keys four wavefronts share the work of one step:
+//  * SV (wavefront g):      K in registers; S = Q K^T and P for query tile t, P
+//                           to LDS, dV^T[0:128) += dO^T P;
+//  * VH (wavefront 4 + g):  P of tile t - 1 from LDS, dV^T[128:256) += dO^T P;
+//  * PK (wavefront 2 + g):  V in registers; dP = dO V^T and dS = P (dP - D) for
+//                           tile t - 1, dS to LDS, dK^T[0:128) += Q^T dS;
+//  * KH (wavefront 6 + g):  dS of tile t - 2 from LDS, dK^T[128:256) += Q^T dS.
+// Wavefronts w and w + 4 share a SIMD, so each SIMD carries one role that
+// holds K or V (24 MFMAs a step) and one that does not (8 MFMAs).  The lags
+// keep one barrier per step: Q tiles are held four deep (t + 1 loading, t, t - 1,
+// t - 2), dO and the row statistics three deep, P and dS two deep.  The
+// products, and the order of every accumulation, are those of the kernel above
+// (32-row Q / dO tiles, 64 keys per work-group: the ten tiles take 130 KiB of LDS).
+struct Dkdv256 {
+    static constexpr int kWaves = 8;
+    static constexpr int kGroups = 2;
+    static constexpr int kKeyBlock = kGroups * kKeysPerWave;
+    static constexpr int kRowTile = 32;
+    static constexpr int kPChunks = 2;
+    static constexpr int kThreads = kWaves * kWave;
+};
+
+// store_tokens for one half of d (four 32-wide d tiles); dst_row points at the half.
+template <typename E>
+__device__ __forceinline__ void store_tokens_half(uint16_t *dst_row, const f32x16 (&acc)[4], float mul, int hh)
+{
+    using e4 = typename V16<E>::x4;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x4 v4 = {acc[dt][4 * a + 0] * mul, acc[dt][4 * a + 1] * mul, acc[dt][4 * a + 2] * mul,
+                              acc[dt][4 * a + 3] * mul};
+            *reinterpret_cast<e4 *>(dst_row + 32 * dt + 8 * a + 4 * hh) = __builtin_convertvector(v4, e4);
+        }
+}
+
+template <bool MASKED, typename E, bool DROPOUT>
+__global__ __launch_bounds__(Dkdv256::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dkdv256_kernel(BwdParams p)
+{
+    constexpr int D = 256;
+    using T = BTile<D>;
+    using S = Dkdv256;
+    using e8 = typename V16<E>::x8;
+    constexpr int kDc = D / 16;
+    constexpr int kRowTile = S::kRowTile;
+    constexpr int kKeyBlock = S::kKeyBlock;
+    constexpr int kTileElems = kRowTile * T::kLdsD;
+    constexpr int kPElems = S::kGroups * S::kPChunks * kWave;
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ2[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ3[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sO0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sO1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sO2[kTileElems];
+    __shared__ __attribute__((aligned(1024))) e8 sP0[kPElems];
+    __shared__ __attribute__((aligned(1024))) e8 sP1[kPElems];
+    __shared__ __attribute__((aligned(1024))) e8 sS0[kPElems];     // dS
+    __shared__ __attribute__((aligned(1024))) e8 sS1[kPElems];
+    __shared__ __attribute__((aligned(256))) float sStat0[128];
+    __shared__ __attribute__((aligned(256))) float sStat1[128];
+    __shared__ __attribute__((aligned(256))) float sStat2[128];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int grp = wave & 1;                       // 32-key group
+    const bool k_side = (wave & 2) != 0;            // PK / KH (dK) or SV / VH (dV)
+    const bool heavy = wave < 4;                    // SV / PK: K or V in registers
+
+    const int n_bh = p.B * p.H;
+    const int bh = blockIdx.x % n_bh;
+    const int kb = blockIdx.x / n_bh;
+    const int kw0 = kb * kKeyBlock + grp * kKeysPerWave;
+    const int key = kw0 + l32;
+    int t0 = 0, t_end = (p.Lq + kRowTile - 1) / kRowTile, wt0 = 0, wt_end = t_end;
+    if (MASKED) {
+        const int64_t k_first = (int64_t)kb * kKeyBlock;
+        const int64_t k_last = min(k_first + kKeyBlock - 1, (int64_t)p.Lk - 1);
+        const int64_t q_lo = p.wr < 0 ? 0 : max((int64_t)0, k_first - p.wr);
+        const int64_t q_hi = p.wl < 0 ? p.Lq : min((int64_t)p.Lq, k_last + p.wl + 1);
+        t0 = t_end = 0;
+        if (q_hi > q_lo) {
+            t0 = (int)(q_lo / kRowTile);
+            t_end = (int)((q_hi + kRowTile - 1) / kRowTile);
+        }
+        const int64_t wq_lo = p.wr < 0 ? 0 : max((int64_t)0, (int64_t)kw0 - p.wr);
+        const int64_t wq_hi = p.wl < 0 ? p.Lq : min((int64_t)p.Lq, (int64_t)kw0 + kKeysPerWave + p.wl);
+        wt0 = max(t0, (int)(wq_lo / kRowTile));
+        wt_end = min(t_end, (int)((wq_hi + kRowTile - 1) / kRowTile));
+    }
+
+    const size_t row_off = (size_t)bh * p.Lq;
+    const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.q) + row_off * D), 0, p.Lq * T::kGRowBytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.dout) + row_off * D), 0, p.Lq * T::kGRowBytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rL = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.lse2 + row_off), 0, p.Lq * 4, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.delta + row_off), 0, p.Lq * 4, kRawBufferFlags);
+
+    // Tile t: Q in slot (t - t0) % 4, dO and the statistics (lse2 at 0, D at 64)
+    // in slot (t - t0) % 3.
+    auto qbuf = [&](int t) {
+        const int s = (t - t0) & 3;
+        return s == 0 ? sQ0 : s == 1 ? sQ1 : s == 2 ? sQ2 : sQ3;
+    };
+    auto obuf = [&](int t) {
+        const int s = (t - t0) % 3;
+        return s == 0 ? sO0 : s == 1 ? sO1 : sO2;
+    };
+    auto sbuf = [&](int t) {
+        const int s = (t - t0) % 3;
+        return s == 0 ? sStat0 : s == 1 ? sStat1 : sStat2;
+    };
+    auto load = [&](int t) {
+        load_tile<D, kRowTile, S::kWaves>(rQ, t * kRowTile, qbuf(t), wave, lane);
+        load_tile<D, kRowTile, S::kWaves>(rO, t * kRowTile, obuf(t), wave, lane);
+        if (wave == 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (LDS_AS void *)(sbuf(t)), 4, 4 * (t * kRowTile + lane), 0, 0, 0);
+        if (wave == 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (LDS_AS void *)(sbuf(t) + 64), 4, 4 * (t * kRowTile + lane),
+                                                     0, 0, 0);
+    };
+    if (t0 < t_end) load(t0);
+
+    // K (SV) or V (PK) of this lane's key as B operands; zero past Lk.
+    e8 xf[kDc];
+    if (heavy) {
+        const uint16_t *Xr = static_cast<const uint16_t *>(k_side ? p.v : p.k) + ((size_t)bh * p.Lk + key) * D;
+#pragma unroll
+        for (int c = 0; c < kDc; ++c)
+            xf[c] = load_row_chunk<E>(Xr + 16 * c + 8 * hh, key < p.Lk);
+    }
+    const ColsOffsets<D> coff = cols_offsets<D>(lane);
+    const int dt0 = heavy ? 0 : 4;                  // this wavefront's half of d
+    f32x16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        acc[t] = f32x16{};
+    const float c2 = p.scale_log2;
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    const int last = t_end + 1;                     // KH finishes tile t_end - 1 at step t_end + 1
+    if (heavy && !k_side) {                         // SV
+        for (int t = t0; t <= last; ++t) {
+            if (t + 1 < t_end) load(t + 1);
+            if (t >= wt0 && t < wt_end) {
+                const LDS_AS char *qb = (const LDS_AS char *)qbuf(t);
+                const LDS_AS char *ob = (const LDS_AS char *)obuf(t);
+                const LDS_AS float *st = (const LDS_AS float *)sbuf(t);
+                f32x16 s = f32x16{};
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    s = mfma_32x32x16(read_rows_op<D, E>(qb, l32, c, hh), xf[c], s);
+                const bool need_mask =
+                    MASKED && !((p.wl < 0 || (int64_t)kw0 >= (int64_t)t * kRowTile + kRowTile - 1 - p.wl) &&
+                                (p.wr < 0 || (int64_t)kw0 + kKeysPerWave - 1 <= (int64_t)t * kRowTile + p.wr));
+                LDS_AS e8 *pdst = (LDS_AS e8 *)((t & 1) ? sP1 : sP0) + grp * S::kPChunks * kWave;
+                DropMask mk;
+                if (DROPOUT) mk.y[0] = mask_key_lanes_one(p.drop, t * kRowTile, 0, key, lane, bh);
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
+                    const int i0 = 8 * c;
+                    const f32x4 l4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 4 * hh);
+                    const f32x4 l4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 16 * c + 8 + 4 * hh);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        s[i0 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i0 + e], c2, -(e < 4 ? l4a[e] : l4b[e - 4])));
+                }
+                if (need_mask) {
+                    const int64_t r_lo = p.wr >= 0 ? (int64_t)key - p.wr : INT64_MIN / 2;
+                    const int64_t r_hi = p.wl >= 0 ? (int64_t)key + p.wl : INT64_MAX / 2;
+                    keep_range(s, (int64_t)t * kRowTile + 4 * hh, r_lo, r_hi, 0.f);
+                }
+                e8 pf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
+                    f32x8 v8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        v8[e] = s[8 * c + e];
+                        if (DROPOUT && !keep(mk, 0, 8 * c + e, p.drop.threshold)) v8[e] = -v8[e];
+                    }
+                    pf[c] = __builtin_convertvector(v8, e8);
+                    pdst[c * kWave + lane] = pf[c];
+                    if (DROPOUT) {
+                        typedef short s8 __attribute__((ext_vector_type(8)));
+                        const s8 bits = __builtin_bit_cast(s8, pf[c]);
+                        pf[c] = __builtin_bit_cast(e8, __builtin_elementwise_max(bits, s8{}));
+                    }
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int c = 0; c < S::kPChunks; ++c)
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, coff, dt, c), pf[c], acc[dt]);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    } else if (!k_side) {                           // VH
+        for (int t = t0; t <= last; ++t) {
+            if (t + 1 < t_end) load(t + 1);
+            const int tv = t - 1;
+            if (tv >= wt0 && tv < wt_end) {
+                const LDS_AS char *ob = (const LDS_AS char *)obuf(tv);
+                const LDS_AS e8 *psrc = (const LDS_AS e8 *)((tv & 1) ? sP1 : sP0) + grp * S::kPChunks * kWave;
+                e8 pf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
+                    pf[c] = psrc[c * kWave + lane];
+                    if (DROPOUT) {
+                        typedef short s8 __attribute__((ext_vector_type(8)));
+                        const s8 bits = __builtin_bit_cast(s8, pf[c]);
+                        pf[c] = __builtin_bit_cast(e8, __builtin_elementwise_max(bits, s8{}));
+                    }
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int c = 0; c < S::kPChunks; ++c)
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, coff, 4 + dt, c), pf[c], acc[dt]);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    } else if (heavy) {                             // PK
+        for (int t = t0; t <= last; ++t) {
+            if (t + 1 < t_end) load(t + 1);
+            const int tk = t - 1;
+            if (tk >= wt0 && tk < wt_end) {
+                const LDS_AS char *qb = (const LDS_AS char *)qbuf(tk);
+                const LDS_AS char *ob = (const LDS_AS char *)obuf(tk);
+                const LDS_AS float *st = (const LDS_AS float *)sbuf(tk);
+                f32x16 dp = f32x16{};
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    dp = mfma_32x32x16(read_rows_op<D, E>(ob, l32, c, hh), xf[c], dp);
+                const LDS_AS e8 *psrc = (const LDS_AS e8 *)((tk & 1) ? sP1 : sP0) + grp * S::kPChunks * kWave;
+                LDS_AS e8 *ddst = (LDS_AS e8 *)((tk & 1) ? sS1 : sS0) + grp * S::kPChunks * kWave;
+                e8 dsf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
+                    const int i0 = 8 * c;
+                    const e8 pc = psrc[c * kWave + lane];
+                    const f32x4 d4a = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 4 * hh);
+                    const f32x4 d4b = *reinterpret_cast<const LDS_AS f32x4 *>(st + 64 + 16 * c + 8 + 4 * hh);
+                    f32x8 v8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float dl = e < 4 ? d4a[e] : d4b[e - 4];
+                        if (DROPOUT) {
+                            const float pr = (float)pc[e];
+                            v8[e] = __builtin_fabsf(pr) * (__builtin_signbit(pr) ? -dl : dp[i0 + e] - dl);
+                        } else {
+                            v8[e] = (float)pc[e] * (dp[i0 + e] - dl);
+                        }
+                    }
+                    dsf[c] = __builtin_convertvector(v8, e8);
+                    ddst[c * kWave + lane] = dsf[c];
+                }
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int c = 0; c < S::kPChunks; ++c)
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, coff, dt, c), dsf[c], acc[dt]);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    } else {                                        // KH
+        for (int t = t0; t <= last; ++t) {
+            if (t + 1 < t_end) load(t + 1);
+            const int tq = t - 2;
+            if (tq >= wt0 && tq < wt_end) {
+                const LDS_AS char *qb = (const LDS_AS char *)qbuf(tq);
+                const LDS_AS e8 *dsrc = (const LDS_AS e8 *)((tq & 1) ? sS1 : sS0) + grp * S::kPChunks * kWave;
+                e8 dsf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c)
+                    dsf[c] = dsrc[c * kWave + lane];
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int c = 0; c < S::kPChunks; ++c)
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, coff, 4 + dt, c), dsf[c], acc[dt]);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    }
+
+    if (key >= p.Lk) return;
+    const size_t kv_row = (size_t)bh * p.Lk + key;
+    uint16_t *dst = static_cast<uint16_t *>(k_side ? p.dk : p.dv) + kv_row * D + 32 * dt0;
+    const float mul = k_side ? (DROPOUT ? p.scale * p.drop.keep_scale : p.scale) : (DROPOUT ? p.drop.keep_scale : 1.0f);
+    store_tokens_half<E>(dst, acc, mul, hh);
+}
+
 // ---------------------------------------------------------------- 3. dQ
 // Probabilities of one 32-key score tile (keys x this lane's query, first key
 // k0; entry i is key k0 + 8(i/4) + 4hh + i%4) set to 0 where the key is past Lk
@@ -761,14 +1069,25 @@ hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const voi
                        const_cast<float *>(p.lse2), const_cast<float *>(p.delta), rows,
                        DROPOUT ? 1.0f / p.drop.keep_scale : 1.0f);
     BwdParams pk = p;
-    pk.n_blocks = (p.Lk + DkdvShape<D>::kKeyBlock - 1) / DkdvShape<D>::kKeyBlock;
-    pk.n_wg = pk.n_blocks * p.B * p.H;
-    if (masked)
-        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true, E, DROPOUT>), dim3(pk.n_wg), dim3(DkdvShape<D>::kThreads), 0,
-                           stream, pk);
-    else
-        hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false, E, DROPOUT>), dim3(pk.n_wg), dim3(DkdvShape<D>::kThreads), 0,
-                           stream, pk);
+    if constexpr (D == 256) {
+        pk.n_blocks = (p.Lk + Dkdv256::kKeyBlock - 1) / Dkdv256::kKeyBlock;
+        pk.n_wg = pk.n_blocks * p.B * p.H;
+        if (masked)
+            hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<true, E, DROPOUT>), dim3(pk.n_wg), dim3(Dkdv256::kThreads), 0,
+                               stream, pk);
+        else
+            hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<false, E, DROPOUT>), dim3(pk.n_wg), dim3(Dkdv256::kThreads), 0,
+                               stream, pk);
+    } else {
+        pk.n_blocks = (p.Lk + DkdvShape<D>::kKeyBlock - 1) / DkdvShape<D>::kKeyBlock;
+        pk.n_wg = pk.n_blocks * p.B * p.H;
+        if (masked)
+            hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, true, E, DROPOUT>), dim3(pk.n_wg), dim3(DkdvShape<D>::kThreads),
+                               0, stream, pk);
+        else
+            hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, false, E, DROPOUT>), dim3(pk.n_wg), dim3(DkdvShape<D>::kThreads),
+                               0, stream, pk);
+    }
     BwdParams pq = p;
     pq.n_blocks = (p.Lq + kBr - 1) / kBr;
     pq.n_wg = pq.n_blocks * p.B * p.H;
