@@ -853,13 +853,13 @@ __device__ __forceinline__ void mask_hidden(f32x16 &pt, int k0, int qrow, int hh
     keep_range(pt, (int64_t)k0 + 4 * hh, lo, hi, 0.f);
 }
 
-// d = 256: Q, dO and the dQ accumulator take 256 registers, so that instance runs
-// one wavefront per SIMD with the accumulation registers in use (and one
-// work-group per CU: 128 KiB of LDS), as the d = 256 forward.
+// d = 256: Q, dO and the dQ accumulator would take 256 registers;
+// fa2_bwd_dq256_kernel below splits the work between wavefront pairs instead.
 template <int D, bool MASKED, typename E, bool DROPOUT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 256 ? 1 : 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa2_bwd_dq_kernel(BwdParams p)
 {
+    static_assert(D <= 128, "d = 256 runs fa2_bwd_dq256_kernel");
     using T = BTile<D>;
     using e8 = typename V16<E>::x8;
     constexpr int kDc = D / 16;
@@ -1059,6 +1059,226 @@ void fa2_bwd_dq_kernel(BwdParams p)
                        hh);
 }
 
+// d = 256 dQ with two wavefronts per SIMD: for each group of 32 query rows a
+// pair of wavefronts, on one SIMD, splits the work of a 32-key tile step:
+//  * X (wavefront g):     Q in registers; S and P for key tile j (P to LDS in
+//                         fp32, the dropout keep bit in its sign), dQ^T[0:128)
+//                         += K^T dS^T for tile j - 2;
+//  * Y (wavefront 4 + g): dO in registers; dP for tile j - 1, P from LDS,
+//                         dS = P (dP - D) to LDS, dQ^T[128:256) += K^T dS^T.
+// K tiles are held four deep (j + 1 loading, j, j - 1, j - 2), V three deep, P
+// and dS two deep: one barrier per step, 160 KiB of LDS.  The products, the fp32
+// P in dS and the order of every accumulation are those of fa2_bwd_dq_kernel, so
+// dQ is bitwise the same.
+struct Dq256 {
+    static constexpr int kWaves = 8;
+    static constexpr int kPairs = 4;
+    static constexpr int kTileKeys = 32;
+    static constexpr int kPChunks = 2;
+    static constexpr int kThreads = kWaves * kWave;
+};
+
+template <bool MASKED, typename E, bool DROPOUT>
+__global__ __launch_bounds__(Dq256::kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa2_bwd_dq256_kernel(BwdParams p)
+{
+    constexpr int D = 256;
+    using T = BTile<D>;
+    using S = Dq256;
+    using e8 = typename V16<E>::x8;
+    constexpr int kDc = D / 16;
+    constexpr int kBk = S::kTileKeys;
+    constexpr int kTileElems = kBk * T::kLdsD;
+    constexpr int kPElems = S::kPairs * S::kPChunks * kWave;
+    __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK2[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK3[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV0[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV1[kTileElems];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV2[kTileElems];
+    __shared__ __attribute__((aligned(1024))) f32x8 sP0[kPElems];   // P in fp32
+    __shared__ __attribute__((aligned(1024))) f32x8 sP1[kPElems];
+    __shared__ __attribute__((aligned(1024))) e8 sS0[kPElems];     // dS
+    __shared__ __attribute__((aligned(1024))) e8 sS1[kPElems];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int pair = wave & 3;
+    const bool is_x = wave < 4;
+
+    int bh, qt;
+    map_workgroup(blockIdx.x, p.n_wg, p.n_blocks, bh, qt);
+    // 32-key tiles [t0, t0 + n_kv) hold a key some row of the block sees.
+    int t0 = 0, n_kv = (p.Lk + kBk - 1) / kBk;
+    if (MASKED) {
+        const int q_first = qt * kBr;
+        const int q_last = min(q_first + kBr - 1, p.Lq - 1);
+        const int64_t key_lo = p.wl < 0 ? 0 : max((int64_t)0, (int64_t)q_first - p.wl);
+        const int64_t key_hi = p.wr < 0 ? p.Lk : min((int64_t)p.Lk, (int64_t)q_last + p.wr + 1);
+        n_kv = 0;
+        if (key_hi > key_lo) {
+            t0 = (int)(key_lo / kBk);
+            n_kv = (int)((key_hi + kBk - 1) / kBk) - t0;
+        }
+    }
+
+    const size_t kv_off = (size_t)bh * p.Lk * D;
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.k) + kv_off), 0, p.Lk * T::kGRowBytes, kRawBufferFlags);
+    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const uint16_t *>(p.v) + kv_off), 0, p.Lk * T::kGRowBytes, kRawBufferFlags);
+
+    const int q0 = qt * kBr + pair * kRowsPerWave;
+    const int qrow = q0 + l32;
+    const bool row_ok = qrow < p.Lq;
+    const bool pair_active = q0 < p.Lq;
+
+    // Tiles this pair computes, counted from t0: [0, n_wave); those in
+    // [plain_lo, n_plain) are seen whole by every row of the pair.
+    int n_wave = 0, n_plain = 0, plain_lo = 0;
+    if (pair_active) {
+        const int pair_qlast = min(q0 + kRowsPerWave - 1, p.Lq - 1);
+        int64_t end = t0 + n_kv, first_plain = 0, end_plain = p.Lk / kBk;
+        if (MASKED) {
+            if (p.wr >= 0) end = min(end, ((int64_t)pair_qlast + p.wr) / kBk + 1);
+            const int64_t left = p.wl < 0 ? 0 : (int64_t)pair_qlast - p.wl;
+            first_plain = left <= 0 ? 0 : (left + kBk - 1) / kBk;
+            if (p.wr >= 0) end_plain = min(end_plain, ((int64_t)q0 + p.wr + 1) / kBk);
+        }
+        n_wave = (int)max(end - t0, (int64_t)0);
+        plain_lo = (int)min(max(first_plain - t0, (int64_t)0), (int64_t)n_wave);
+        n_plain = (int)min(max(end_plain - t0, (int64_t)0), (int64_t)n_wave);
+    }
+
+    // Local tile j (global t0 + j): K in slot j % 4, V in slot j % 3.
+    auto kbuf = [&](int j) {
+        const int s = j & 3;
+        return s == 0 ? sK0 : s == 1 ? sK1 : s == 2 ? sK2 : sK3;
+    };
+    auto vbuf = [&](int j) {
+        const int s = j % 3;
+        return s == 0 ? sV0 : s == 1 ? sV1 : sV2;
+    };
+    auto load = [&](int j) {
+        load_tile<D, kBk, S::kWaves>(rK, (t0 + j) * kBk, kbuf(j), wave, lane);
+        load_tile<D, kBk, S::kWaves>(rV, (t0 + j) * kBk, vbuf(j), wave, lane);
+    };
+    if (n_kv > 0) load(0);
+
+    // Q (X) or dO (Y) of this lane's row as B operands; zero past Lq.
+    const size_t qoff = (size_t)bh * p.Lq + qrow;
+    const uint16_t *Rr = static_cast<const uint16_t *>(is_x ? p.q : p.dout) + qoff * D;
+    e8 rf[kDc];
+#pragma unroll
+    for (int c = 0; c < kDc; ++c)
+        rf[c] = load_row_chunk<E>(Rr + 16 * c + 8 * hh, row_ok);
+    const float stat = row_ok ? (is_x ? p.lse2[qoff] : p.delta[qoff]) : 0.f;   // lse2 (X) or D (Y)
+    const ColsOffsets<D> coff = cols_offsets<D>(lane);
+    const int dt0 = is_x ? 0 : 4;
+    f32x16 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        acc[t] = f32x16{};
+    const float c2 = p.scale_log2;
+
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // dQ^T[half] += K^T dS^T over the tile's 32 keys (B operands dsf).
+    auto dq_update = [&](const LDS_AS char *kb, const e8 (&dsf)[S::kPChunks]) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int c = 0; c < S::kPChunks; ++c)
+                acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kb, coff, dt0 + dt, c), dsf[c], acc[dt]);
+    };
+    const int last = n_kv + 1;                      // X finishes its dQ of tile n_kv - 1 at step n_kv + 1
+    if (is_x) {
+        for (int j = 0; j <= last; ++j) {
+            if (j + 1 < n_kv) load(j + 1);
+            if (j < n_wave) {
+                // S^T = K Q^T (keys x this pair's queries), P = 2^(S c - lse2).
+                const LDS_AS char *kb = (const LDS_AS char *)kbuf(j);
+                f32x16 s = f32x16{};
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    s = mfma_32x32x16(read_rows_op<D, E>(kb, l32, c, hh), rf[c], s);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -stat));
+                if (j < plain_lo || j >= n_plain) mask_hidden<MASKED>(s, (t0 + j) * kBk, qrow, hh, p);
+                u32x4 y = {};
+                if (DROPOUT) y = mask_query_lanes_one(p.drop, (t0 + j) * kBk, 0, qrow, lane, bh);
+                LDS_AS f32x8 *pdst = (LDS_AS f32x8 *)((j & 1) ? sP1 : sP0) + pair * S::kPChunks * kWave;
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
+                    f32x8 v8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int i = 8 * c + e;
+                        v8[e] = s[i];
+                        if (DROPOUT && ((y[i / 4] >> (8 * (i % 4))) & 0xFFu) >= p.drop.threshold) v8[e] = -v8[e];
+                    }
+                    pdst[c * kWave + lane] = v8;
+                }
+            }
+            const int jq = j - 2;
+            if (jq >= 0 && jq < n_wave) {
+                const LDS_AS e8 *dsrc = (const LDS_AS e8 *)((jq & 1) ? sS1 : sS0) + pair * S::kPChunks * kWave;
+                e8 dsf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c)
+                    dsf[c] = dsrc[c * kWave + lane];
+                dq_update((const LDS_AS char *)kbuf(jq), dsf);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    } else {
+        for (int j = 0; j <= last; ++j) {
+            if (j + 1 < n_kv) load(j + 1);
+            const int jk = j - 1;
+            if (jk >= 0 && jk < n_wave) {
+                // dP^T = V dO^T, dS = P (dP - D) (dropout: dS / ks with D / ks).
+                const LDS_AS char *vb = (const LDS_AS char *)vbuf(jk);
+                f32x16 dp = f32x16{};
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    dp = mfma_32x32x16(read_rows_op<D, E>(vb, l32, c, hh), rf[c], dp);
+                const LDS_AS f32x8 *psrc = (const LDS_AS f32x8 *)((jk & 1) ? sP1 : sP0) + pair * S::kPChunks * kWave;
+                LDS_AS e8 *ddst = (LDS_AS e8 *)((jk & 1) ? sS1 : sS0) + pair * S::kPChunks * kWave;
+                e8 dsf[S::kPChunks];
+#pragma unroll
+                for (int c = 0; c < S::kPChunks; ++c) {
+                    const f32x8 pc = psrc[c * kWave + lane];
+                    f32x8 v8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float pr = pc[e];
+                        if (DROPOUT)
+                            v8[e] = __builtin_fabsf(pr) * (__builtin_signbit(pr) ? -stat : dp[8 * c + e] - stat);
+                        else
+                            v8[e] = pr * (dp[8 * c + e] - stat);
+                    }
+                    dsf[c] = __builtin_convertvector(v8, e8);
+                    ddst[c * kWave + lane] = dsf[c];
+                }
+                dq_update((const LDS_AS char *)kbuf(jk), dsf);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    }
+
+    if (!row_ok) return;
+    store_tokens_half<E>(static_cast<uint16_t *>(p.dq) + qoff * D + 32 * dt0, acc,
+                         DROPOUT ? p.scale * p.drop.keep_scale : p.scale, hh);
+}
+
 template <int D, typename E, bool DROPOUT = false>
 hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const void *o, const float *lse,
                         hipStream_t stream)
@@ -1091,8 +1311,13 @@ hipError_t launch_bwd_d(const BwdParams &p, bool masked, int64_t rows, const voi
     BwdParams pq = p;
     pq.n_blocks = (p.Lq + kBr - 1) / kBr;
     pq.n_wg = pq.n_blocks * p.B * p.H;
-    if (masked) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true, E, DROPOUT>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
-    else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false, E, DROPOUT>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    if constexpr (D == 256) {
+        if (masked) hipLaunchKernelGGL((fa2_bwd_dq256_kernel<true, E, DROPOUT>), dim3(pq.n_wg), dim3(Dq256::kThreads), 0, stream, pq);
+        else        hipLaunchKernelGGL((fa2_bwd_dq256_kernel<false, E, DROPOUT>), dim3(pq.n_wg), dim3(Dq256::kThreads), 0, stream, pq);
+    } else {
+        if (masked) hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, true, E, DROPOUT>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+        else        hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, false, E, DROPOUT>), dim3(pq.n_wg), dim3(kThreads), 0, stream, pq);
+    }
     return hipGetLastError();
 }
 
