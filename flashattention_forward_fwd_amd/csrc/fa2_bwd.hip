@@ -23,7 +23,9 @@
 //     (fa2_bwd_dkdv256_kernel), so two wavefronts still share a SIMD.
 //  3. dQ: one work-group per tile of 128 query rows, laid out like the forward
 //     kernel: each wavefront keeps Q and dO of its 32 rows in registers and
-//     accumulates dQ^T while 64-key tiles of K and V stream through LDS.
+//     accumulates dQ^T while 64-key tiles of K and V stream through LDS.  d =
+//     256: a wavefront pair per 32 rows, one holding Q, one dO, each
+//     accumulating half of dQ^T over 32-key tiles (fa2_bwd_dq256_kernel).
 // dQ is computed by its own pass (S and dP rebuilt a second time) instead of
 // being accumulated across key blocks with atomics, which would make the sum
 // order, and so the rounding, depend on scheduling.
