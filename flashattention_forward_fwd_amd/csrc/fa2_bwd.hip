@@ -184,6 +184,25 @@ __device__ __forceinline__ typename V16<E>::x8 read_cols_op(const LDS_AS char *t
     return __builtin_bit_cast(typename V16<E>::x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// The same operand at a lane offset computed beforehand: row l32 (+ 32 rows for
+// the second half) and logical chunk 16c + 8hh are BTile::addr(l32, 2 (16c + 8hh))
+// + 32 h rows, since the swizzle depends on the row's low four bits only.
+template <typename E>
+__device__ __forceinline__ typename V16<E>::x8 read_rows_at(const LDS_AS char *tile, int off)
+{
+    return *reinterpret_cast<const LDS_AS typename V16<E>::x8 *>(tile + off);
+}
+
+// x unchanged, but opaque to the optimiser at this point of the program: per-lane
+// LDS offsets re-issued inside a loop are added to the (constant) buffer address
+// at each use, which folds into the instruction's offset field, instead of one
+// register per (buffer, offset) pair being kept across the loop.
+__device__ __forceinline__ int opaque(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // 16 bytes of a 16-bit row from global memory (zero when `valid` is false).
 template <typename E>
 __device__ __forceinline__ typename V16<E>::x8 load_row_chunk(const uint16_t *p, bool valid)
@@ -312,8 +331,9 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     __shared__ __attribute__((aligned(1024))) uint16_t sO1[kTileElems];
     __shared__ __attribute__((aligned(1024))) uint16_t sO2[kTileElems];
     // P of one tile: [key group][chunk c][lane] x 16 bytes, in the lane order of the B operand
-    __shared__ __attribute__((aligned(1024))) e8 sP0[S::kGroups * S::kPChunks * kWave];
-    __shared__ __attribute__((aligned(1024))) e8 sP1[S::kGroups * S::kPChunks * kWave];
+    // (one array for both buffers: its accesses are known not to touch the tiles
+    // that asynchronous copies are filling)
+    __shared__ __attribute__((aligned(1024))) e8 sP[2][S::kGroups * S::kPChunks * kWave];
     // per buffer: lse2 of the tile's rows at 0, their D at 64 (a 32-row tile
     // leaves the upper halves unused)
     __shared__ __attribute__((aligned(256))) float sStat0[128];
@@ -366,18 +386,16 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
 
     // Tile t lives in buffer set (t - t0) % 3: Q, dO, and lse2 (loaded by wave 0)
     // and D (wave 1) of its 64 rows.
-    auto qbuf = [&](int slot) { return slot == 0 ? sQ0 : slot == 1 ? sQ1 : sQ2; };
-    auto obuf = [&](int slot) { return slot == 0 ? sO0 : slot == 1 ? sO1 : sO2; };
-    auto sbuf = [&](int slot) { return slot == 0 ? sStat0 : slot == 1 ? sStat1 : sStat2; };
-    auto load = [&](int t) {
-        const int slot = (t - t0) % 3;
-        load_tile<D, kRowTile, S::kWaves>(rQ, t * kRowTile, qbuf(slot), wave, lane);
-        load_tile<D, kRowTile, S::kWaves>(rO, t * kRowTile, obuf(slot), wave, lane);
+    // The loops below run three steps per trip, so that every slot is fixed at
+    // compile time.
+    auto load = [&](int t, uint16_t *q, uint16_t *o, float *st) {
+        load_tile<D, kRowTile, S::kWaves>(rQ, t * kRowTile, q, wave, lane);
+        load_tile<D, kRowTile, S::kWaves>(rO, t * kRowTile, o, wave, lane);
         if (wave < 2)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rL : rD, (LDS_AS void *)(sbuf(slot) + 64 * wave),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wave == 0 ? rL : rD, (LDS_AS void *)(st + 64 * wave),
                                                      4, 4 * (t * kRowTile + lane), 0, 0, 0);
     };
-    if (t0 < t_end) load(t0);
+    if (t0 < t_end) load(t0, sQ0, sO0, sStat0);
 
     // K (dV wavefronts) or V (dK wavefronts) of this lane's key as B operands
     // (d chunk 16c + 8hh); zero past Lk.
@@ -388,6 +406,11 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
         xf[c] = load_row_chunk<E>(Xr + 16 * c + 8 * hh, key < p.Lk);
 
     const ColsOffsets<D> coff = cols_offsets<D>(lane);
+    // Lane offsets of the Q and dO rows operands (read_rows_at).
+    int roff[kDc];
+#pragma unroll
+    for (int c = 0; c < kDc; ++c)
+        roff[c] = BTile<D>::addr(l32, 2 * (16 * c + 8 * hh));
     f32x16 acc[kDt];                       // dV^T (wavefronts 0-3) or dK^T (4-7)
 #pragma unroll
     for (int t = 0; t < kDt; ++t)
@@ -402,13 +425,23 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
     // barriers): in one shared loop the register allocator kept the accumulator
     // of the two roles in different registers and copied it on every step.
     if (!is_dk) {
-        for (int t = t0; t <= t_end; ++t) {
-            if (t + 1 < t_end) load(t + 1);
+        auto step = [&](int t, const uint16_t *q, const uint16_t *o, const float *sts, uint16_t *qn, uint16_t *on,
+                        float *stn) {
+            if (t + 1 < t_end) load(t + 1, qn, on, stn);
             if (t >= wt0 && t < wt_end) {
-                const int slot = (t - t0) % 3;
-                const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
-                const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
-                const LDS_AS float *st = (const LDS_AS float *)sbuf(slot);
+                const LDS_AS char *qb = (const LDS_AS char *)q;
+                const LDS_AS char *ob = (const LDS_AS char *)o;
+                const LDS_AS float *st = (const LDS_AS float *)sts;
+                int ro[kDc];
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    ro[c] = opaque(roff[c]);
+                ColsOffsets<D> co;
+#pragma unroll
+                for (int dt = 0; dt < kDt; ++dt) {
+                    co.lo[dt] = opaque(coff.lo[dt]);
+                    co.hi[dt] = opaque(coff.hi[dt]);
+                }
                 // S = Q K^T for the tile's rows (32-row halves h) x this group's 32
                 // keys.  Entry i of half h is row 32h + 8(i/4) + 4hh + i%4.
                 f32x16 s[S::kHalves];
@@ -417,7 +450,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                     s[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        s[h] = mfma_32x32x16(read_rows_op<D, E>(qb, 32 * h + l32, c, hh), xf[c], s[h]);
+                        s[h] = mfma_32x32x16(read_rows_at<E>(qb + 32 * h * T::kRowBytes, ro[c]), xf[c], s[h]);
                 }
                 // Does every (row, key) pair of this tile and key group lie in the window?
                 const bool need_mask =
@@ -425,7 +458,7 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                                 (p.wr < 0 || (int64_t)kw0 + kKeysPerWave - 1 <= (int64_t)t * kRowTile + p.wr));
                 // Chunk c (B operand of the products over the tile's rows) holds
                 // rows 16c + 8(e/4) + 4hh + e%4, e = 0..7: entries 8(c%2) + e of half c/2.
-                LDS_AS e8 *pdst = (LDS_AS e8 *)((t & 1) ? sP1 : sP0) + grp * S::kPChunks * kWave;
+                LDS_AS e8 *pdst = (LDS_AS e8 *)sP[t & 1] + grp * S::kPChunks * kWave;
                 DropMask mk;
                 if (DROPOUT)
 #pragma unroll
@@ -476,20 +509,38 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < S::kPChunks; ++c)
-                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, coff, dt, c), pf[c], acc[dt]);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(ob, co, dt, c), pf[c], acc[dt]);
             }
             __builtin_amdgcn_s_waitcnt(0);    // this wave's loads of tile t+1 have landed
             __syncthreads();                  // ... everyone's; P of tile t is visible; old buffers free
+        };
+        // Tile t is in slot (t - t0) % 3.
+        for (int t = t0; t <= t_end; t += 3) {
+            step(t, sQ0, sO0, sStat0, sQ1, sO1, sStat1);
+            if (t + 1 <= t_end) step(t + 1, sQ1, sO1, sStat1, sQ2, sO2, sStat2);
+            if (t + 2 <= t_end) step(t + 2, sQ2, sO2, sStat2, sQ0, sO0, sStat0);
         }
     } else {
-        for (int t = t0; t <= t_end; ++t) {
-            if (t + 1 < t_end) load(t + 1);
+        // Step t works on tile tk = t - 1, in slot (tk - t0) % 3, and loads tile
+        // t + 1 into slot (t + 1 - t0) % 3.
+        auto step = [&](int t, const uint16_t *q, const uint16_t *o, const float *sts, uint16_t *qn, uint16_t *on,
+                        float *stn) {
+            if (t + 1 < t_end) load(t + 1, qn, on, stn);
             const int tk = t - 1;
             if (tk >= wt0 && tk < wt_end) {
-                const int slot = (tk - t0) % 3;
-                const LDS_AS char *qb = (const LDS_AS char *)qbuf(slot);
-                const LDS_AS char *ob = (const LDS_AS char *)obuf(slot);
-                const LDS_AS float *st = (const LDS_AS float *)sbuf(slot);
+                const LDS_AS char *qb = (const LDS_AS char *)q;
+                const LDS_AS char *ob = (const LDS_AS char *)o;
+                const LDS_AS float *st = (const LDS_AS float *)sts;
+                int ro[kDc];
+#pragma unroll
+                for (int c = 0; c < kDc; ++c)
+                    ro[c] = opaque(roff[c]);
+                ColsOffsets<D> co;
+#pragma unroll
+                for (int dt = 0; dt < kDt; ++dt) {
+                    co.lo[dt] = opaque(coff.lo[dt]);
+                    co.hi[dt] = opaque(coff.hi[dt]);
+                }
                 // dP = dO V^T, same layout as S.
                 f32x16 dp[S::kHalves];
 #pragma unroll
@@ -497,9 +548,9 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                     dp[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        dp[h] = mfma_32x32x16(read_rows_op<D, E>(ob, 32 * h + l32, c, hh), xf[c], dp[h]);
+                        dp[h] = mfma_32x32x16(read_rows_at<E>(ob + 32 * h * T::kRowBytes, ro[c]), xf[c], dp[h]);
                 }
-                const LDS_AS e8 *psrc = (const LDS_AS e8 *)((tk & 1) ? sP1 : sP0) + grp * S::kPChunks * kWave;
+                const LDS_AS e8 *psrc = (const LDS_AS e8 *)sP[tk & 1] + grp * S::kPChunks * kWave;
                 e8 dsf[S::kPChunks];
 #pragma unroll
                 for (int c = 0; c < S::kPChunks; ++c) {
@@ -525,10 +576,15 @@ void fa2_bwd_dkdv_kernel(BwdParams p)
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < S::kPChunks; ++c)
-                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, coff, dt, c), dsf[c], acc[dt]);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(qb, co, dt, c), dsf[c], acc[dt]);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
+        };
+        for (int t = t0; t <= t_end; t += 3) {
+            step(t, sQ2, sO2, sStat2, sQ1, sO1, sStat1);
+            if (t + 1 <= t_end) step(t + 1, sQ0, sO0, sStat0, sQ2, sO2, sStat2);
+            if (t + 2 <= t_end) step(t + 2, sQ1, sO1, sStat1, sQ0, sO0, sStat0);
         }
     }
 
@@ -946,6 +1002,11 @@ void fa2_bwd_dq_kernel(BwdParams p)
     const float lse2 = row_ok ? p.lse2[qoff] : 0.f;
     const float dlt = row_ok ? p.delta[qoff] : 0.f;
     const ColsOffsets<D> coff = cols_offsets<D>(lane);
+    // Lane offsets of the K and V rows operands (read_rows_at).
+    int roff[kDc];
+#pragma unroll
+    for (int c = 0; c < kDc; ++c)
+        roff[c] = BTile<D>::addr(l32, 2 * (16 * c + 8 * hh));
 
     f32x16 acc[kDt];
 #pragma unroll
@@ -956,14 +1017,28 @@ void fa2_bwd_dq_kernel(BwdParams p)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int j = 0; j < n_kv; ++j) {
-        const bool odd = j & 1;
+    // One step per K/V tile; the loop runs two steps per trip so that every
+    // buffer is fixed at compile time.
+    auto step = [&](int j, const uint16_t *sKc, const uint16_t *sVc, uint16_t *sKn, uint16_t *sVn) {
         if (j + 1 < n_kv) {
-            load_tile<D, kBc>(rK, (t0 + j + 1) * kBc, odd ? sK0 : sK1, wave, lane);
-            load_tile<D, kBc>(rV, (t0 + j + 1) * kBc, odd ? sV0 : sV1, wave, lane);
+            load_tile<D, kBc>(rK, (t0 + j + 1) * kBc, sKn, wave, lane);
+            load_tile<D, kBc>(rV, (t0 + j + 1) * kBc, sVn, wave, lane);
         }
-        const LDS_AS char *kbuf = (const LDS_AS char *)(odd ? sK1 : sK0);
-        const LDS_AS char *vbuf = (const LDS_AS char *)(odd ? sV1 : sV0);
+        const LDS_AS char *kbuf = (const LDS_AS char *)sKc;
+        const LDS_AS char *vbuf = (const LDS_AS char *)sVc;
+        int ro[kDc];
+#pragma unroll
+        for (int c = 0; c < kDc; ++c)
+            ro[c] = opaque(roff[c]);
+        ColsOffsets<D> co;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) {
+            co.lo[dt] = opaque(coff.lo[dt]);
+            co.hi[dt] = opaque(coff.hi[dt]);
+        }
+        auto rows_op = [&](const LDS_AS char *tile, int t, int c) {
+            return read_rows_at<E>(tile + 32 * t * BTile<D>::kRowBytes, ro[c]);
+        };
         if (j < n_wave) {
             // Entry i of score tile t is key 64(t0 + j) + 32t + 8(i/4) + 4hh + i%4.
             const bool need_mask = j < plain_lo || j >= n_plain;
@@ -975,10 +1050,10 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     dp_t = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        s_t = mfma_32x32x16(read_rows_op<D, E>(kbuf, 32 * t + l32, c, hh), qf[c], s_t);
+                        s_t = mfma_32x32x16(rows_op(kbuf, t, c), qf[c], s_t);
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        dp_t = mfma_32x32x16(read_rows_op<D, E>(vbuf, 32 * t + l32, c, hh), of[c], dp_t);
+                        dp_t = mfma_32x32x16(rows_op(vbuf, t, c), of[c], dp_t);
                 };
                 // dS / ks of half t (dlt = D / ks, keep bytes y of that half) as the B
                 // operands of key chunks 2t, 2t + 1.
@@ -1014,7 +1089,7 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                         for (int h = 0; h < 2; ++h)
-                            acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, coff, dt, 2 * t + h), dsf[h], acc[dt]);
+                            acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, co, dt, 2 * t + h), dsf[h], acc[dt]);
                 }
             } else {
                 // S^T = K Q^T and dP^T = V dO^T: (keys x this wavefront's queries).
@@ -1025,10 +1100,10 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     dp[t] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        s[t] = mfma_32x32x16(read_rows_op<D, E>(kbuf, 32 * t + l32, c, hh), qf[c], s[t]);
+                        s[t] = mfma_32x32x16(rows_op(kbuf, t, c), qf[c], s[t]);
 #pragma unroll
                     for (int c = 0; c < kDc; ++c)
-                        dp[t] = mfma_32x32x16(read_rows_op<D, E>(vbuf, 32 * t + l32, c, hh), of[c], dp[t]);
+                        dp[t] = mfma_32x32x16(rows_op(vbuf, t, c), of[c], dp[t]);
                 }
                 // P = 2^(S c - lse2) in place; hidden pairs -> 0 under one branch per
                 // tile (the same on every lane).
@@ -1056,11 +1131,15 @@ void fa2_bwd_dq_kernel(BwdParams p)
                 for (int dt = 0; dt < kDt; ++dt)
 #pragma unroll
                     for (int c = 0; c < 4; ++c)
-                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, coff, dt, c), dsf[c], acc[dt]);
+                        acc[dt] = mfma_32x32x16(read_cols_op<D, E>(kbuf, co, dt, c), dsf[c], acc[dt]);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    };
+    for (int j = 0; j < n_kv; j += 2) {
+        step(j, sK0, sV0, sK1, sV1);
+        if (j + 1 < n_kv) step(j + 1, sK1, sV1, sK0, sV0);
     }
 
     if (!row_ok) return;
