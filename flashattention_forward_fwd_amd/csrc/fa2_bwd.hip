@@ -1105,6 +1105,16 @@ void fa2_bwd_dq_kernel(BwdParams p)
                     for (int c = 0; c < kDc; ++c)
                         dp[t] = mfma_32x32x16(rows_op(vbuf, t, c), of[c], dp[t]);
                 }
+                // Pin the order of these 32 reads and products so that each read is
+                // issued two products ahead (the compiler's own schedule read each
+                // operand just before its product and waited out the full LDS latency).
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int i = 0; i < 4 * kDc - 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                 // P = 2^(S c - lse2) in place; hidden pairs -> 0 under one branch per
                 // tile (the same on every lane).
 #pragma unroll
