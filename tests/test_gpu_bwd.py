@@ -81,6 +81,21 @@ def test_bwd_parity_ragged(shape, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
+def test_bwd_loop_trip_counts(n, d, causal):
+    """The dK/dV loop runs three steps per trip (ceil(Lq / 64) + 1 steps in all)
+    and the dQ loop two (ceil(Lk / 64) steps): lengths 64 n - 5 for n = 1..6 give
+    every remainder of both, each with a ragged last tile."""
+    L = 64 * n - 5
+    seed = 500 + 10 * n + d + causal
+    q, k, v = random_qkv(1, 2, L, L, d, "bf16", seed=seed)
+    do = random_dout(1, 2, L, d, "bf16", seed=seed)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(d)))
+    check_full("bwd trips n=%d d=%d" % (n, d), q, k, v, do, causal, scale)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_bwd_parity_large_score_range(causal):
     """Q x 4: peaky rows, probabilities near 0 and 1."""
     q, k, v = random_qkv(1, 2, 300, 450, 128, "bf16", seed=77, q_mult=4.0)
