@@ -190,6 +190,45 @@ def test_dropout_backward_parity(case):
     check_bwd("dropout bwd", q, k, v, do, causal, float(np.float32(1 / np.sqrt(d))), p, 0xC0FFEE + Lk, Lq)
 
 
+@pytest.mark.parametrize("case", [
+    # Lq, d, p, inputs seed, dropout seed, offset
+    (65, 64, 0.1, 2015, 5487277651644988878, 72267039),
+    (200, 128, 0.3, 7, 0xABCDEF, 5),
+    (129, 32, 0.5, 8, 0x13579BDF, 77),
+], ids=lambda c: "Lq%d-d%d-p%g" % c[:3])
+def test_dropout_backward_single_key(case):
+    """One key: P = 1 on every row, so dS = P (dP - D) and with it dQ and dK vanish
+    exactly.  The backward forms D = rowsum(dO * O) from the forward's stored 16-bit
+    O ("FlashAttention 怎么做? online softmax 怎么更新?", section "Recomputation"),
+    and under dropout O = V * 256 / t is not a bf16 value, so what the device returns
+    here is the rounding of O carried through D -- an error on the scale of
+    |dO| |O|, not of the (zero) gradient.  Checked against that quantity in float64:
+    the same formulas with D taken from O rounded to bf16 (nearest even)."""
+    Lq, d, p, in_seed, seed, offset = case
+    q, k, v = random_qkv(1, 1, Lq, 1, d, "bf16", seed=in_seed)
+    do = random_dout(1, 1, Lq, d, "bf16", seed=in_seed)
+    scale = float(np.float32(1 / np.sqrt(d)))
+    t = ref.dropout_threshold(p)
+    ks = 256.0 / t
+    say("case dropout bwd single key Lq=%d d=%d p=%g" % (Lq, d, p))
+    got = run_dropout_bwd(q, k, v, do, False, scale, p, seed, offset)
+    exact = ref.attention_dropout_f64(widen(q), widen(k), widen(v), scale, False, seed, offset, t, dout=widen(do))[2:]
+    Q, K, V, dO = (widen(x)[0, 0] for x in (q, k, v, do))
+    Z = ref.dropout_mask(1, 1, Lq, 1, seed, offset, t)[0, 0].astype(np.float64)
+    A = Z * ks                                            # P = 1
+    O16 = torch.from_numpy(A @ V).to(torch.bfloat16).double().numpy()
+    D = np.sum(dO * O16, axis=1, keepdims=True)
+    dS = A / ks * (dO @ V.T * A - D)                     # P (dP - D), dP = dO V^T * Z * ks
+    model = (scale * dS @ K, scale * dS.T @ Q)
+    for gname, g, e, m in zip(("dq", "dk"), got[:2], exact[:2], model):
+        g = g[0, 0]
+        err = float(np.max(np.abs(g - m)))
+        bar = 5e-2 * float(np.abs(m).max()) + 1e-3
+        say("  %s max|G| %.3e (exact %.1e)  max|G - model| %.3e (bar %.3e)" % (
+            gname, float(np.abs(g).max()), float(np.abs(e).max()), err, bar))
+        assert float(np.abs(e).max()) < 1e-9 and err <= bar, gname
+
+
 def test_dropout_backward_zero_rate_is_plain_backward():
     q, k, v = (x.cuda() for x in random_qkv(1, 2, 300, 300, 128, "bf16", seed=8))
     do = random_dout(1, 2, 300, 128, "bf16", seed=8).cuda()
